@@ -1,0 +1,331 @@
+"""Benchmark of the fused AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variants all|none|LIST]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+One timed step is one pass of the whole path over a 268,435,456-element flat
+FP32 bucket (FP32 gradients, steady state at t = 1000, moments pre-warmed):
+gradient statistics (radamw_grad_stats), the hierarchical fan-in-1024 merge
+(radamw_merge_stats), the 12-byte report read back to the host
+(radamw_read_report, the step's one synchronisation), the skip / clip
+decision (radamw_decide, global norm clipped at 1.0), and the in-place fused
+update (radamw_step_multi over the bucket).  Inputs are resident in HBM
+before the timer starts.  HIP events recorded on the launch stream around
+every update and statistics launch inside the timed region give the
+per-kernel durations the roofline object uses.
+
+Prints ONE JSON line (rank 0).  Extra keys beside the contract's:
+"roofline", "cpu_baseline", "kernels" (per-kernel event timings),
+"variants" (update-only timings of the other configurations of the bucket),
+"copy_ceiling" (torch device-to-device copy bandwidth, context only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "fused AdamW step params/s + achieved HBM GB/s (% of peak), 268M FP32"
+N_BUCKET = 268_435_456
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_PARAM = {  # algorithmic bytes moved per element by one update
+    ("adamw", "f32", False): 28, ("adamw", "bf16", False): 26, ("adamw", "f16", False): 26,
+    ("amsgrad", "f32", False): 36, ("amsgrad", "bf16", False): 34, ("amsgrad", "f16", False): 34,
+    ("adamw", "f32", True): 20, ("amsgrad", "f32", True): 24,
+}
+PROFILE_COUNTERS = os.path.join(HERE, "profiles", "update_adamw_f32_268M_counters.md")
+KERNEL_SOURCES = [os.path.join(HERE, "optimizer_step_dl_amd", "csrc", f)
+                  for f in ("radamw_update.hip", "radamw_internal.h")]
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_from_profile():
+    """HBM bytes per update dispatch from the committed rocprofv3 counter
+    summary, scaled by the copy-kernel calibration recorded with it; None if
+    absent or taken on a different kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    vals = dict(re.findall(r"^- ([a-z_0-9]+): ([0-9A-Za-z.+\-e]+)\s*$", text, flags=re.M))
+    try:
+        if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(vals["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_inputs(torch, synth, n, variant, gdt, device):
+    """Config-3 bucket: p ~ N(0, 0.02), g ~ N(0, 1e-3), m ~ N(0, 1e-4),
+    v = N(0, 1e-3)^2, v_max = v * U(1, 1.5); drawn on the device."""
+    key = (0, "bucket", n)
+    p = synth.normal(n, 0.02, key + ("p",), device)
+    g = synth.stored_grad(n, 1e-3, 1.0, gdt, key + ("g",), device)
+    m, v, vmax = synth.steady_state(n, key, variant == "amsgrad", device, m_std=1e-4, v_root_std=1e-3)
+    return p, g, m, v, vmax
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--n", type=int, default=N_BUCKET)
+    ap.add_argument("--variants", default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB torch copy (the counter calibration kernel)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py: this build runs the optimizer step on one GPU only; "
+                         "--gpus above 1 is not supported (see the sharding design notes).\n")
+        return 2
+
+    import torch
+    import synth
+    import optimizer_step_dl_amd as ra
+    from optimizer_step_dl_amd import _abi
+
+    lib = ra.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    n = args.n
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs, n={n}")
+
+    # ---------------------------------------------------- headline step --
+    p, g, m, v, _ = build_inputs(torch, synth, n, "adamw", "f32", dev)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    step = ctypes.c_uint64(999)
+    seg = (_abi._Segment * 1)(_abi._Segment(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), None, n))
+    rows_n = lib.radamw_grad_stats_rows(n, 0)
+    se, ex = ra.radamw_stats_plan(rows_n)
+    rows = torch.zeros(3 * rows_n, dtype=torch.int32, device=dev)
+    scratch = torch.zeros(max(se, 1), dtype=torch.float32, device=dev)
+    report = torch.zeros(3, dtype=torch.int32, device=dev)
+    host_report = _abi.Stats()
+    written = ctypes.c_int64()
+    ctrl = _abi.Control()
+    result = _abi.FusedResult()
+    updated = ctypes.c_int32()
+    max_norm = 1.0
+    check = lambda rc, w: rc == 0 or (_ for _ in ()).throw(ra.RadamwError(rc, w))
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.radamw_grad_stats(g.data_ptr(), 0, n, rows.data_ptr(), rows_n, ctypes.byref(written), sptr),
+              "grad_stats")
+        check(lib.radamw_merge_stats(rows.data_ptr(), rows_n, scratch.data_ptr(), se, report.data_ptr(), 1, sptr),
+              "merge_stats")
+        if ev is not None:
+            ev[1].record(stream)
+        check(lib.radamw_read_report(report.data_ptr(), ctypes.byref(host_report), sptr), "read_report")
+        check(lib.radamw_decide(ctypes.byref(host_report), 1.0, max_norm, ctypes.byref(ctrl),
+                                ctypes.byref(result)), "decide")
+        if ctrl.skip_update:
+            raise RuntimeError("unexpected non-finite gradient in the benchmark bucket")
+        if ev is not None:
+            ev[2].record(stream)
+        check(lib.radamw_step_multi(seg, 1, 0, ctypes.byref(step), ctypes.byref(opts), ctypes.byref(ctrl), sptr,
+                                    ctypes.byref(updated)), "step_multi")
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    upd_ms = [e[2].elapsed_time(e[3]) for e in events]
+    stats_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    value = n / (ms_per_step * 1e-3)
+    upd_avg = sum(upd_ms) / len(upd_ms)
+    stats_avg = sum(stats_ms) / len(stats_ms)
+    bpp = BYTES_PER_PARAM[("adamw", "f32", False)]
+    achieved = bpp * n / (upd_avg * 1e-3) / 1e9
+    traffic = counters_from_profile()
+    log(f"step {ms_per_step:.3f} ms, update {upd_avg:.3f} ms ({achieved:.0f} GB/s), stats+merge {stats_avg:.3f} ms, "
+        f"clip {result.clip_coef:.4f}, norm {result.total_norm:.4f}")
+    kernels = {
+        "update_adamw_f32_inplace": {"avg_ms": upd_avg, "min_ms": min(upd_ms), "max_ms": max(upd_ms),
+                                     "bytes_per_param": bpp, "gbs": achieved},
+        "grad_stats_plus_merge": {"avg_ms": stats_avg, "min_ms": min(stats_ms), "max_ms": max(stats_ms),
+                                  "bytes_per_param": 4, "gbs": 4 * n / (stats_avg * 1e-3) / 1e9,
+                                  "rows": rows_n, "extra_merge_kernels": ex},
+    }
+    del p, g, m, v, rows, scratch
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------ update-only variants --
+    wanted = [] if args.variants == "none" else (
+        ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
+         "adamw_f32_firststep"] if args.variants == "all" else args.variants.split(","))
+    variants = {}
+    for name in wanted:
+        variant, gdt, mode = name.split("_")
+        first = mode == "firststep"
+        amsgrad = variant == "amsgrad"
+        p, g, m, v, vmax = build_inputs(torch, synth, n, variant, gdt, dev)
+        o = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
+        c = ra.control(1.0)
+        st_step = 0 if first else 999
+        if mode == "outofplace":
+            outs = [torch.empty_like(p), torch.empty_like(m), torch.empty_like(v),
+                    torch.empty_like(vmax) if amsgrad else None]
+            sets = [(p, m, v, vmax), tuple(outs)]
+
+            def launch(k):
+                a, b = sets[k % 2], sets[(k + 1) % 2]
+                sin = ra.AdamWState(st_step + k, a[1], a[2], a[3])
+                sout = ra.AdamWState(0, b[1], b[2], b[3])
+                ra.radamw_step(a[0], g, sin, o, c, b[0], sout)
+        else:
+            def launch(k):
+                st = ra.AdamWState(0 if first else st_step + k, m, v, vmax)
+                ra.radamw_step_inplace(p, g, st, o, c)
+        for k in range(3):
+            launch(k)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for k, (a, b) in enumerate(ev):
+            a.record(stream)
+            launch(k)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        avg = sum(ms) / len(ms)
+        bp = BYTES_PER_PARAM[(variant, gdt, first)]
+        variants[name] = {"avg_ms": avg, "min_ms": min(ms), "bytes_per_param": bp,
+                          "params_per_s": n / (avg * 1e-3), "gbs": bp * n / (avg * 1e-3) / 1e9,
+                          "frac_of_peak": bp * n / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"variant {name}: {avg:.3f} ms, {variants[name]['gbs']:.0f} GB/s")
+        del p, g, m, v, vmax
+        if mode == "outofplace":
+            del outs, sets
+        torch.cuda.empty_cache()
+
+    # --------------------------------------------------- copy ceiling --
+    copy_ceiling = None
+    if args.copy_calibration or wanted:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / 10
+        copy_ceiling = {"bytes": 2 * a.numel() * 4, "avg_ms": cms, "gbs": 2 * a.numel() * 4 / (cms * 1e-3) / 1e9}
+        log(f"copy ceiling: {copy_ceiling['gbs']:.0f} GB/s")
+        del a, b
+
+    # --------------------------------------------------- CPU oracle --
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, synth, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal draws on the device)",
+        "config": {
+            "workload": (f"flat bucket of {n:,} FP32 params, FP32 grads, AdamW lr 1e-3 betas (0.9,0.999) eps 1e-5 "
+                         "wd 1e-4, steady state from t=1000, in place; step = grad stats + hierarchical merge + "
+                         "12-byte read-back + global-norm clip at 1.0 + fused update"),
+            "n_params": n, "grad_dtype": "f32", "optimizer": "adamw", "storage": "in-place",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "adamw_update_single<f32, adamw, steady>",
+                     "algorithmic_bytes_per_launch": bpp * n},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "variants": variants,
+        "copy_ceiling": copy_ceiling,
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+                   "torch": torch.__version__, "hip": torch.version.hip},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(torch, synth, seconds):
+    """The oracle's full step (statistics, decision, update) on a bounded
+    sample of the same bucket: the first 2^24 elements, drawn on the CPU with
+    the same recipe; repeated until `seconds` have passed.  One core."""
+    import numpy as np
+    import oracle
+    n = 1 << 24
+    key = (0, "bucket-cpu", n)
+    p = synth.normal(n, 0.02, key + ("p",)).numpy().copy()
+    g = synth.grad_numpy(synth.stored_grad(n, 1e-3, 1.0, "f32", key + ("g",)))
+    m, v, _ = synth.steady_state(n, key, False)
+    st = oracle.State.__new__(oracle.State)
+    st.step, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq = 999, m.numpy().copy(), v.numpy().copy(), None
+    opts = oracle.Options(lr=1e-3, weight_decay=1e-4)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        sumsq, count = oracle.grad_stats(g, "f32")
+        skip, eff = oracle.decide(sumsq, count, 1.0, 1.0)
+        oracle.adamw_step(p, g, "f32", st, opts, eff, skip)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"cpu oracle: {steps} steps of {n} elements in {el:.1f} s")
+    return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first 2^24 = {n:,} elements of the same bucket recipe (CPU draws), full step "
+                      f"(stats + decision + update), {steps} steps in {el:.1f} s, single thread",
+            "bytes_per_param_model": 28}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,319 @@
+/*
+ * radamw.h -- C ABI of libradamw.so, the fused AdamW / AMSGrad optimizer
+ * step for AMD Instinct MI355X (gfx950).
+ *
+ * Page abbreviations used in the citations below:
+ *   FA-ja  = RUDA docs page "実験的なデバイス上の融合 AdamW / AMSGrad"
+ *   FA-zh  = RUDA docs page "实验性融合 AdamW / AMSGrad"
+ *   TR-zh  = RUDA docs page "训练与状态保存"
+ *
+ * General conventions (all entry points):
+ *   - Every array pointer is a DEVICE pointer (hipMalloc / torch CUDA
+ *     memory) unless the argument says "host".  Host pointers are rejected
+ *     (FA-ja "サポートされている契約": no arbitrary host pointers).
+ *   - Arrays are dense and contiguous, 1-D, indexed 0..n-1.  Parameters and
+ *     moments are FP32; gradients are FP32, FP16 or BF16 (FA-zh
+ *     "增加的实际能力").  Pointers must be aligned to their element size.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     legacy default stream) and is asynchronous: a RADAMW_OK return means
+ *     the work was SUBMITTED, not that it completed (FA-ja "低レベルの使用").
+ *     The caller keeps every buffer alive until the stream has passed the
+ *     work, and synchronises before reading results or saving a checkpoint.
+ *   - Any non-zero return other than RADAMW_ERR_HIP means nothing was
+ *     launched and nothing (device memory, state structs, step counts,
+ *     output flags) was modified (FA-ja "低レベルの使用": validation leaves
+ *     every input unchanged).  RADAMW_ERR_HIP reports a failing HIP runtime
+ *     call; a multi-kernel entry point may have submitted earlier kernels,
+ *     and the caller should treat the device state as unconfirmed (FA-ja
+ *     "低レベルの使用": discard unconfirmed outputs after a device fault).
+ *     The library keeps no pointer after a call returns.
+ *   - There is no device-side step counter: the completed-step count lives
+ *     in host memory owned by the caller, and the bias-correction
+ *     coefficients are computed on the host for every call, so a captured
+ *     graph replay would repeat one step's coefficients (FA-zh
+ *     "增加的实际能力"); graph capture is not supported.
+ *   - Thread safety: calls may come from several host threads; each call is
+ *     independent apart from the launch counter and the per-device caches
+ *     of the segment-table path, which are internally locked.
+ */
+#ifndef RADAMW_H
+#define RADAMW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without requiring the HIP headers in C callers. */
+typedef struct ihipStream_t *radamw_stream_t;
+
+/* ----------------------------------------------------------- status codes */
+enum {
+    RADAMW_OK = 0,
+    RADAMW_ERR_INVALID = -1, /* null pointer, n < 0, unknown dtype, host pointer,
+                                hyper-parameter out of range, non-finite or
+                                non-positive gradient_scale, flag not 0/1     */
+    RADAMW_ERR_STATE = -2,   /* AMSGrad flag and v_max presence disagree, or
+                                the step count would overflow                 */
+    RADAMW_ERR_ALIAS = -3,   /* a written range overlaps another range         */
+    RADAMW_ERR_ALIGN = -4,   /* pointer not aligned to its element size        */
+    RADAMW_ERR_RANGE = -5,   /* row count / capacity / scratch size out of range */
+    RADAMW_ERR_HIP = -6      /* a HIP runtime call failed (see
+                                radamw_last_hip_error)                         */
+};
+
+/* Gradient storage type (FA-zh "增加的实际能力"). */
+typedef enum {
+    RADAMW_F32 = 0,
+    RADAMW_F16 = 1,  /* IEEE binary16 */
+    RADAMW_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+} radamw_dtype;
+
+/*
+ * Hyper-parameters of the update (FA-ja "この演算子を使用する理由": formula
+ * and defaults; FA-ja "低レベルの使用": the options struct).  Checked:
+ * lr >= 0, eps >= 0, weight_decay >= 0, 0 <= beta1, beta2 < 1, all finite;
+ * amsgrad and maximize are 0 or 1.
+ */
+typedef struct {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int32_t amsgrad;
+    int32_t maximize;
+} radamw_options;
+
+/*
+ * Per-call control (FA-ja "低レベルの使用": StepControl).  The stored
+ * gradient is divided by gradient_scale (finite, > 0).  skip_update = 1 is
+ * the caller's found_inf decision: no launch, no write, no step increment
+ * (FA-zh "增加的实际能力").  The library never scans for non-finite values
+ * inside the update itself.
+ */
+typedef struct {
+    double gradient_scale;
+    int32_t skip_update;
+} radamw_control;
+
+/*
+ * Optimizer state of one tensor (FA-ja "低レベルの使用": the state exposes
+ * the step and the moment buffers).  step is the number of completed
+ * updates; step == 0 is the pages' "no state yet": the next update is t = 1
+ * and initialises the moments inside the kernel without reading them
+ * (FA-zh "增加的实际能力").  exp_avg / exp_avg_sq / max_exp_avg_sq are
+ * device FP32 arrays of n elements; max_exp_avg_sq is non-NULL exactly when
+ * AMSGrad is on.
+ */
+typedef struct {
+    uint64_t step;
+    float *exp_avg;
+    float *exp_avg_sq;
+    float *max_exp_avg_sq;
+} radamw_state;
+
+/* One contiguous tensor of a multi-tensor update (in place). */
+typedef struct {
+    float *param;
+    const void *grad;
+    float *exp_avg;
+    float *exp_avg_sq;
+    float *max_exp_avg_sq; /* NULL unless AMSGrad */
+    int64_t n;
+} radamw_segment;
+
+/*
+ * 12-byte gradient-statistics record (TR-zh "在 ruda:0 上进行原生 PyTorch
+ * 训练": a 12-byte report is read back before the update).  Layout chosen
+ * here (the pages fix only the size): w[0] | w[1] << 32 is the IEEE binary64
+ * sum of squares of the finite stored gradient values; w[2] is the count of
+ * non-finite values, saturating at 2^32 - 1.  The same record is used for
+ * the per-workgroup rows, the intermediate merge levels and the report.
+ */
+typedef struct {
+    uint32_t w[3];
+} radamw_stats;
+
+/* Result of radamw_fused_step_multi (host struct). */
+typedef struct {
+    int32_t updated;     /* 1 when the update was launched                  */
+    int32_t found_inf;   /* 1 when the report counted non-finite values     */
+    uint32_t nonfinite;  /* the report's non-finite count                   */
+    uint32_t reserved;
+    double sumsq;        /* the report's sum of squares (stored scale)      */
+    double total_norm;   /* sqrt(sumsq) / gradient_scale                    */
+    double clip_coef;    /* min(1, max_norm / (total_norm + 1e-6)), or 1    */
+} radamw_fused_result;
+
+/* Defaults of FA-ja "この演算子を使用する理由": betas (0.9, 0.999),
+ * eps 1e-5, weight decay 1e-4; lr 1e-3 as in the pages' usage examples;
+ * amsgrad = maximize = 0.  Returns the struct by value. */
+radamw_options radamw_options_default(void);
+
+/*
+ * Out-of-place update of one tensor (FA-ja "低レベルの使用": adamw_step;
+ * FA-ja "割り当てとパフォーマンスのモデル": out-of-place outputs).
+ *   p, g      : inputs, n elements; g has dtype gdt.  Never written.
+ *   in        : host struct; in->step completed steps.  When in->step == 0
+ *               the input moment pointers are not read (may be NULL).
+ *   p_out     : output params (device, n FP32), caller-allocated.
+ *   out       : host struct with caller-allocated output moment arrays
+ *               (n FP32 each; max_exp_avg_sq iff amsgrad).  On launch,
+ *               out->step = in->step + 1; otherwise out is not touched.
+ *   updated   : host int32, set to 1 on launch, 0 on skip / n == 0.
+ * No output range may overlap any input or other output (RADAMW_ERR_ALIAS).
+ * skip_update or n == 0: nothing is launched or written (FA-zh
+ * "增加的实际能力"), so the caller may allocate outputs only after a call
+ * with ctrl->skip_update known to be 0.
+ */
+int radamw_step(const float *p, const void *g, radamw_dtype gdt, int64_t n,
+                const radamw_state *in, float *p_out, radamw_state *out,
+                const radamw_options *opts, const radamw_control *ctrl,
+                radamw_stream_t stream, int32_t *updated);
+
+/*
+ * In-place update over caller-owned storage (FA-ja "ネイティブ PyTorch
+ * ストレージと階層統計": the storage kernel adamw_scaled).  p, st->exp_avg,
+ * st->exp_avg_sq (and st->max_exp_avg_sq iff AMSGrad) are read and written;
+ * g is read only.  st->step is incremented only when the kernel is launched.
+ */
+int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
+                        radamw_state *st, const radamw_options *opts,
+                        const radamw_control *ctrl, radamw_stream_t stream,
+                        int32_t *updated);
+
+/*
+ * In-place update of a list of tensors that share one options struct and
+ * one step count, in ONE kernel launch (FA-ja "サポートされている契約": a
+ * pre-flattened bucket works only when every element shares the options and
+ * the step count).  A flattened bucket is nseg == 1.
+ *   segs  : host array of nseg descriptors (device pointers inside).
+ *   step  : host, the shared completed-step count; incremented on launch.
+ * Segments with n == 0 are ignored; when every segment is empty nothing is
+ * launched and *step is unchanged.  No written range may overlap any other
+ * range of any segment (RADAMW_ERR_ALIAS).  nseg >= 0.
+ */
+int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt,
+                      uint64_t *step, const radamw_options *opts,
+                      const radamw_control *ctrl, radamw_stream_t stream,
+                      int32_t *updated);
+
+/*
+ * Merge plan for rows statistics records (FA-ja "ネイティブ PyTorch
+ * ストレージと階層統計": StatsPlan; TR-zh "在 ruda:0 上进行原生 PyTorch
+ * 训练": fan-in 1024, at most two extra merge kernels, at most 49,200 bytes
+ * of reusable scratch).  rows must be in 1..4,194,304 (else
+ * RADAMW_ERR_RANGE).  *scratch_elements receives the FP32-element count of
+ * the intermediate levels (3 per record; initial rows and final report not
+ * included); *extra_merge_kernels the number of fan-in-1024 levels before
+ * the final merge (0 when rows <= 1024).  Host only; no device access.
+ */
+int radamw_stats_plan(int64_t rows, int64_t *scratch_elements,
+                      int32_t *extra_merge_kernels);
+
+/* Number of records one radamw_grad_stats call writes for n elements of
+ * dtype gdt (a deterministic function of n and gdt alone; 0 when n == 0).
+ * Returns a negative status for n < 0 or an unknown dtype.  Host only. */
+int64_t radamw_grad_stats_rows(int64_t n, radamw_dtype gdt);
+
+/*
+ * Read-only analysis of one gradient (FA-ja "ネイティブ PyTorch ストレージと
+ * 階層統計": analyze_gradient; TR-zh: gradient storage stays unchanged).
+ * Writes radamw_grad_stats_rows(n, gdt) records to rows_out (device), each
+ * the sum of squares of the finite values and the non-finite count of one
+ * workgroup's share.  rows_capacity < that count -> RADAMW_ERR_RANGE.
+ * *rows_written (host) receives the count (0 when n == 0: nothing launched).
+ * The reduction order is fixed, so repeated calls give identical bits.
+ */
+int radamw_grad_stats(const void *g, radamw_dtype gdt, int64_t n,
+                      radamw_stats *rows_out, int64_t rows_capacity,
+                      int64_t *rows_written, radamw_stream_t stream);
+
+/*
+ * Reduce nrows records to the 12-byte report (FA-ja "ネイティブ PyTorch
+ * ストレージと階層統計": merge_gradient_stats_chunks then
+ * merge_gradient_stats; TR-zh: hierarchical fan-in 1024 changes only the
+ * reduction order).  nrows in 1..4,194,304.
+ *   hierarchical = 1: the radamw_stats_plan levels, each reducing groups of
+ *     up to 1024 records into scratch, then one final merge into report.
+ *     scratch (device, FP32 elements, 4-byte aligned) must hold
+ *     scratch_elements >= the plan's count; it may be NULL when that count
+ *     is 0.
+ *   hierarchical = 0: one final merge over all rows (scratch unused).
+ * Counts are bit-identical between the two modes; sums differ only by
+ * FP64 rounding order.  report: 12 device bytes owned by the caller.
+ */
+int radamw_merge_stats(const radamw_stats *rows, int64_t nrows, float *scratch,
+                       int64_t scratch_elements, radamw_stats *report,
+                       int32_t hierarchical, radamw_stream_t stream);
+
+/*
+ * Read a device report back to the host (hipMemcpyAsync through a pinned
+ * staging buffer, then stream synchronisation).  This is the one place the
+ * step waits for the device (TR-zh: the report is read back before any
+ * update).  host_report: host struct.
+ */
+int radamw_read_report(const radamw_stats *report, radamw_stats *host_report,
+                       radamw_stream_t stream);
+
+/*
+ * Host decision after the report (TR-zh "在 ruda:0 上进行原生 PyTorch 训练":
+ * any non-finite gradient skips the whole step; optional global L2 clipping
+ * after unscaling).  norm = sqrt(sumsq) / gradient_scale; clip = min(1,
+ * max_grad_norm / (norm + 1e-6)) when max_grad_norm > 0, else 1.
+ * Fills ctrl: skip_update = (count > 0); gradient_scale = gradient_scale /
+ * clip (exactly gradient_scale when clip == 1).  result (optional, may be
+ * NULL) receives the decoded report and the decision.  Host only.
+ */
+int radamw_decide(const radamw_stats *host_report, double gradient_scale,
+                  double max_grad_norm, radamw_control *ctrl,
+                  radamw_fused_result *result);
+
+/*
+ * The whole fused step over a tensor list, the ruda_torch.AdamW
+ * fused_step path of TR-zh: statistics of every active gradient ->
+ * (hierarchical) merge -> 12-byte report read back -> skip or clip decision
+ * -> one in-place radamw_step_multi launch.
+ *   workspace : device, >= radamw_fused_workspace_bytes(...) bytes, 4-byte
+ *               aligned, caller-owned (rows, merge scratch and report).
+ *   max_grad_norm <= 0 disables clipping.
+ *   result    : host struct, always filled on RADAMW_OK.
+ * Synchronises the stream once (the report read-back).
+ */
+int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg,
+                                     radamw_dtype gdt);
+int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
+                            radamw_dtype gdt, uint64_t *step,
+                            const radamw_options *opts, double gradient_scale,
+                            double max_grad_norm, int32_t hierarchical,
+                            void *workspace, int64_t workspace_bytes,
+                            radamw_stream_t stream, radamw_fused_result *result);
+
+/*
+ * The FP32 constants one update launches with, formed on the host in FP64
+ * and cast (FA-ja "この演算子を使用する理由": bias corrections by an FP64
+ * integer power, cast to FP32), for update number t >= 1:
+ *   out9 = {beta1, 1 - beta1, beta2, 1 - beta2, (maximize ? -1 : 1) /
+ *           gradient_scale, 1 - lr * weight_decay, lr / (1 - beta1^t),
+ *           1 / (1 - beta2^t), eps}.
+ * Host only (out9: host array of 9 floats); lets the coefficients be
+ * checked without a device.
+ */
+int radamw_host_coefficients(const radamw_options *opts, uint64_t t, double gradient_scale,
+                             float *out9);
+
+/* Utilities. */
+const char *radamw_status_string(int status);
+/* Last HIP error code seen by this thread inside the library (0 = none). */
+int radamw_last_hip_error(void);
+/* Total kernel launches made by the library in this process (test hook:
+ * proves skip / empty calls launch nothing). */
+uint64_t radamw_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RADAMW_H */

@@ -1,0 +1,794 @@
+// radamw_api.cpp -- the C ABI of libradamw.so: validation, host-side
+// coefficients, launch geometry, segment tables and the statistics plan.
+//
+// Page abbreviations: FA-ja = RUDA docs page "実験的なデバイス上の融合 AdamW /
+// AMSGrad"; FA-zh = "实验性融合 AdamW / AMSGrad"; TR-zh = "训练与状态保存".
+//
+// Every entry point validates all of its arguments before it launches or
+// writes anything (FA-ja "低レベルの使用"), so a failed call has no effect.
+#include "radamw.h"
+#include "radamw_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+using namespace radamw;
+
+namespace {
+
+std::atomic<uint64_t> g_launches{0};
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return RADAMW_OK;
+    g_last_hip = static_cast<int>(e);
+    return RADAMW_ERR_HIP;
+}
+
+// ------------------------------------------------------------ device info --
+
+constexpr int MAX_DEVICES = 64;
+
+struct DeviceCache {
+    std::mutex mu;
+    int cu_count = 0;
+    // segment-table staging ring (see TableRing below)
+    static constexpr int RING = 8;
+    struct Slot {
+        void *host = nullptr;
+        void *dev = nullptr;
+        size_t cap = 0;
+        hipEvent_t done = nullptr;
+        bool pending = false;
+    } slots[RING];
+    int next = 0;
+    // pinned 12-byte staging for report read-back
+    radamw_stats *pinned_report = nullptr;
+};
+
+DeviceCache g_devices[MAX_DEVICES];
+
+int stream_device(hipStream_t stream, int *dev) {
+    hipDevice_t d = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &d) : hipGetDevice(&d);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        g_last_hip = static_cast<int>(e);
+        return RADAMW_ERR_INVALID;
+    }
+    if (d < 0 || d >= MAX_DEVICES) return RADAMW_ERR_INVALID;
+    *dev = static_cast<int>(d);
+    return RADAMW_OK;
+}
+
+int cu_count(int dev) {
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.mu);
+    if (dc.cu_count == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;  // MI355X
+        }
+        dc.cu_count = cus;
+    }
+    return dc.cu_count;
+}
+
+// ------------------------------------------------------------- validation --
+
+bool is_finite(double x) { return std::isfinite(x); }
+
+int check_options(const radamw_options *o) {
+    if (!o) return RADAMW_ERR_INVALID;
+    if (!is_finite(o->lr) || o->lr < 0.0) return RADAMW_ERR_INVALID;
+    if (!is_finite(o->eps) || o->eps < 0.0) return RADAMW_ERR_INVALID;
+    if (!is_finite(o->weight_decay) || o->weight_decay < 0.0) return RADAMW_ERR_INVALID;
+    if (!(o->beta1 >= 0.0 && o->beta1 < 1.0)) return RADAMW_ERR_INVALID;
+    if (!(o->beta2 >= 0.0 && o->beta2 < 1.0)) return RADAMW_ERR_INVALID;
+    if ((o->amsgrad != 0 && o->amsgrad != 1) || (o->maximize != 0 && o->maximize != 1))
+        return RADAMW_ERR_INVALID;
+    return RADAMW_OK;
+}
+
+int check_scale(double gradient_scale) {
+    return (is_finite(gradient_scale) && gradient_scale > 0.0) ? RADAMW_OK : RADAMW_ERR_INVALID;
+}
+
+int check_control(const radamw_control *c) {
+    if (!c) return RADAMW_ERR_INVALID;
+    if (c->skip_update != 0 && c->skip_update != 1) return RADAMW_ERR_INVALID;
+    return check_scale(c->gradient_scale);
+}
+
+bool valid_dtype(int gdt) { return gdt == RADAMW_F32 || gdt == RADAMW_F16 || gdt == RADAMW_BF16; }
+
+size_t grad_bytes(int gdt) { return gdt == RADAMW_F32 ? 4 : 2; }
+
+// A device (or managed) allocation of `dev`, aligned to `align` bytes.
+int check_device_ptr(const void *p, size_t align, int dev) {
+    if (!p) return RADAMW_ERR_INVALID;
+    if (reinterpret_cast<uintptr_t>(p) % align != 0) return RADAMW_ERR_ALIGN;
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof a);
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // do not leave a sticky error for the caller
+        return RADAMW_ERR_INVALID;
+    }
+    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return RADAMW_ERR_INVALID;
+    if (a.device != dev) return RADAMW_ERR_INVALID;
+    return RADAMW_OK;
+}
+
+// Byte ranges touched by one call.  Written ranges may overlap nothing;
+// read-only ranges may overlap each other.
+struct Range {
+    uintptr_t lo, hi;
+    bool written;
+};
+
+void add_range(std::vector<Range> &v, const void *p, int64_t bytes, bool written) {
+    if (p && bytes > 0) {
+        uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+        v.push_back({lo, lo + static_cast<uintptr_t>(bytes), written});
+    }
+}
+
+// Sweep in start order: a written range must start after every earlier
+// range ended; a read range must start after every earlier written range.
+int check_alias(std::vector<Range> &v) {
+    std::sort(v.begin(), v.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    uintptr_t end_any = 0, end_written = 0;
+    for (const Range &r : v) {
+        if (r.written ? r.lo < end_any : r.lo < end_written) return RADAMW_ERR_ALIAS;
+        end_any = std::max(end_any, r.hi);
+        if (r.written) end_written = std::max(end_written, r.hi);
+    }
+    return RADAMW_OK;
+}
+
+// ----------------------------------------------------------- coefficients --
+
+// beta^t in FP64 by binary exponentiation (an integer power, FA-ja
+// "この演算子を使用する理由").
+double int_pow(double base, uint64_t e) {
+    double r = 1.0;
+    while (e) {
+        if (e & 1) r *= base;
+        base *= base;
+        e >>= 1;
+    }
+    return r;
+}
+
+// FP64 formation and FP32 cast of every per-call constant, once per call.
+Coefs make_coefs(const radamw_options &o, uint64_t t, double gradient_scale) {
+    const double bc1 = 1.0 - int_pow(o.beta1, t);
+    const double bc2 = 1.0 - int_pow(o.beta2, t);
+    Coefs c;
+    c.beta1 = static_cast<float>(o.beta1);
+    c.one_minus_beta1 = static_cast<float>(1.0 - o.beta1);
+    c.beta2 = static_cast<float>(o.beta2);
+    c.one_minus_beta2 = static_cast<float>(1.0 - o.beta2);
+    c.inv_scale = static_cast<float>((o.maximize ? -1.0 : 1.0) / gradient_scale);
+    c.decay = static_cast<float>(1.0 - o.lr * o.weight_decay);
+    c.step_size = static_cast<float>(o.lr / bc1);
+    c.inv_bc2 = static_cast<float>(1.0 / bc2);
+    c.eps = static_cast<float>(o.eps);
+    return c;
+}
+
+// ----------------------------------------------------------- segment geometry
+
+bool same_phase(const void *q, int phase) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(q);
+    return (a & 3) == 0 && static_cast<int>((a >> 2) & 3) == phase;
+}
+
+// Leading scalar elements so that all streams are 16-byte aligned after
+// them, or -1 when the streams' alignments differ.
+int32_t segment_head(const SegDesc &s, int gdt, bool amsgrad, bool first) {
+    const int phase = static_cast<int>((reinterpret_cast<uintptr_t>(s.p_in) >> 2) & 3);
+    bool ok = same_phase(s.p_out, phase) && same_phase(s.m_out, phase) && same_phase(s.v_out, phase);
+    if (amsgrad) ok = ok && same_phase(s.vmax_out, phase);
+    if (!first) {
+        ok = ok && same_phase(s.m_in, phase) && same_phase(s.v_in, phase);
+        if (amsgrad) ok = ok && same_phase(s.vmax_in, phase);
+    }
+    const uintptr_t ga = reinterpret_cast<uintptr_t>(s.g);
+    const int gphase = gdt == RADAMW_F32 ? static_cast<int>((ga >> 2) & 3) : static_cast<int>((ga >> 1) & 3);
+    ok = ok && gphase == phase;
+    if (!ok) return -1;
+    int64_t head = (4 - phase) & 3;
+    if (head > s.n) head = s.n;
+    return static_cast<int32_t>(head);
+}
+
+int update_grid(int dev, int64_t tiles) {
+    const int64_t cap = int64_t(cu_count(dev)) * RADAMW_UPDATE_BLOCKS_PER_CU;
+    return static_cast<int>(std::max<int64_t>(1, std::min(tiles, cap)));
+}
+
+// Validate one tensor's pointers for an update; appends its byte ranges.
+// For an out-of-place call the inputs are read-only ranges and the outputs
+// written ones; in place, the state and parameter ranges are written.
+int check_update_tensor(const SegDesc &s, int gdt, bool amsgrad, bool first, bool inplace, int dev,
+                        std::vector<Range> &ranges) {
+    const int64_t fb = s.n * 4, gb = s.n * static_cast<int64_t>(grad_bytes(gdt));
+    int rc;
+    if (!inplace && (rc = check_device_ptr(s.p_in, 4, dev))) return rc;
+    if ((rc = check_device_ptr(s.g, grad_bytes(gdt), dev))) return rc;
+    if ((rc = check_device_ptr(s.p_out, 4, dev))) return rc;
+    if ((rc = check_device_ptr(s.m_out, 4, dev))) return rc;
+    if ((rc = check_device_ptr(s.v_out, 4, dev))) return rc;
+    if (amsgrad && (rc = check_device_ptr(s.vmax_out, 4, dev))) return rc;
+    if (!first && !inplace) {
+        if ((rc = check_device_ptr(s.m_in, 4, dev))) return rc;
+        if ((rc = check_device_ptr(s.v_in, 4, dev))) return rc;
+        if (amsgrad && (rc = check_device_ptr(s.vmax_in, 4, dev))) return rc;
+    }
+    add_range(ranges, s.g, gb, false);
+    if (inplace) {
+        add_range(ranges, s.p_out, fb, true);
+        add_range(ranges, s.m_out, fb, true);
+        add_range(ranges, s.v_out, fb, true);
+        if (amsgrad) add_range(ranges, s.vmax_out, fb, true);
+    } else {
+        add_range(ranges, s.p_in, fb, false);
+        if (!first) {
+            add_range(ranges, s.m_in, fb, false);
+            add_range(ranges, s.v_in, fb, false);
+            if (amsgrad) add_range(ranges, s.vmax_in, fb, false);
+        }
+        add_range(ranges, s.p_out, fb, true);
+        add_range(ranges, s.m_out, fb, true);
+        add_range(ranges, s.v_out, fb, true);
+        if (amsgrad) add_range(ranges, s.vmax_out, fb, true);
+    }
+    return RADAMW_OK;
+}
+
+int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, int dev,
+                  hipStream_t stream) {
+    s.head = segment_head(s, gdt, amsgrad, first);
+    s.tile_begin = 0;
+    const int grid = update_grid(dev, segment_tiles(s.n, s.head));
+    int rc = hip_status(launch_update_single(s, c, gdt, amsgrad, first, grid, stream));
+    if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
+    return rc;
+}
+
+// Several tensors in one launch: descriptors and tile prefix sums are
+// packed into pinned host memory, copied to a device slot on the caller's
+// stream, and the slot is recycled once an event shows the kernel that read
+// it has finished.
+int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
+                 int dev, hipStream_t stream) {
+    const int32_t nseg = static_cast<int32_t>(segs.size());
+    std::vector<int64_t> prefix(nseg + 1);
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < nseg; ++i) {
+        segs[i].head = segment_head(segs[i], gdt, amsgrad, first);
+        segs[i].tile_begin = tiles;
+        prefix[i] = tiles;
+        tiles += segment_tiles(segs[i].n, segs[i].head);
+    }
+    prefix[nseg] = tiles;
+    const size_t desc_bytes = sizeof(SegDesc) * nseg;
+    const size_t bytes = desc_bytes + sizeof(int64_t) * (nseg + 1);
+
+    DeviceCache &dc = g_devices[dev];
+    const int grid = update_grid(dev, tiles);
+    std::lock_guard<std::mutex> lock(dc.mu);
+    DeviceCache::Slot &slot = dc.slots[dc.next];
+    dc.next = (dc.next + 1) % DeviceCache::RING;
+    if (slot.pending) {
+        hipError_t e = hipEventSynchronize(slot.done);
+        if (e != hipSuccess) return hip_status(e);
+        slot.pending = false;
+    }
+    if (!slot.done) {
+        hipError_t e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    if (slot.cap < bytes) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        if (slot.dev) (void)hipFree(slot.dev);
+        slot.host = slot.dev = nullptr;
+        slot.cap = 0;
+        size_t cap = std::max<size_t>(bytes, 64 * 1024);
+        hipError_t e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_status(e);
+        e = hipMalloc(&slot.dev, cap);
+        if (e != hipSuccess) {
+            (void)hipHostFree(slot.host);
+            slot.host = nullptr;
+            return hip_status(e);
+        }
+        slot.cap = cap;
+    }
+    std::memcpy(slot.host, segs.data(), desc_bytes);
+    std::memcpy(static_cast<char *>(slot.host) + desc_bytes, prefix.data(), sizeof(int64_t) * (nseg + 1));
+    hipError_t e = hipMemcpyAsync(slot.dev, slot.host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_status(e);
+    const SegDesc *d_segs = static_cast<const SegDesc *>(slot.dev);
+    const int64_t *d_prefix = reinterpret_cast<const int64_t *>(static_cast<const char *>(slot.dev) + desc_bytes);
+    e = launch_update_table(d_segs, d_prefix, nseg, tiles, c, gdt, amsgrad, first, grid, stream);
+    if (e != hipSuccess) return hip_status(e);
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    e = hipEventRecord(slot.done, stream);
+    if (e != hipSuccess) return hip_status(e);
+    slot.pending = true;
+    return RADAMW_OK;
+}
+
+// Validated multi-tensor update (shared by radamw_step_multi and the fused step).
+int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *step,
+                 const radamw_options &o, double gradient_scale, int dev, hipStream_t stream,
+                 int32_t *updated) {
+    std::vector<SegDesc> active;
+    active.reserve(nseg);
+    const bool first = (*step == 0);
+    for (int32_t i = 0; i < nseg; ++i) {
+        const radamw_segment &s = segs[i];
+        if (s.n == 0) continue;
+        SegDesc d{};
+        d.p_in = s.param;
+        d.g = s.grad;
+        d.m_in = s.exp_avg;
+        d.v_in = s.exp_avg_sq;
+        d.vmax_in = s.max_exp_avg_sq;
+        d.p_out = s.param;
+        d.m_out = s.exp_avg;
+        d.v_out = s.exp_avg_sq;
+        d.vmax_out = s.max_exp_avg_sq;
+        d.n = s.n;
+        active.push_back(d);
+    }
+    if (active.empty()) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    const Coefs c = make_coefs(o, *step + 1, gradient_scale);
+    int rc = active.size() == 1
+                 ? launch_single(active[0], gdt, o.amsgrad != 0, first, c, dev, stream)
+                 : launch_table(active, gdt, o.amsgrad != 0, first, c, dev, stream);
+    if (rc != RADAMW_OK) return rc;
+    *step += 1;
+    *updated = 1;
+    return RADAMW_OK;
+}
+
+// Validate a segment list for an in-place multi-tensor update.
+int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgrad, bool first,
+                   int dev, int64_t *active_out) {
+    if (nseg < 0 || (nseg > 0 && !segs)) return RADAMW_ERR_INVALID;
+    std::vector<Range> ranges;
+    int64_t active = 0;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const radamw_segment &s = segs[i];
+        if (s.n < 0) return RADAMW_ERR_INVALID;
+        if (s.n == 0) continue;  // empty tensors may carry null pointers
+        if ((s.max_exp_avg_sq != nullptr) != amsgrad) return RADAMW_ERR_STATE;
+        ++active;
+        SegDesc d{};
+        d.p_in = d.p_out = s.param;
+        d.g = s.grad;
+        d.m_in = d.m_out = s.exp_avg;
+        d.v_in = d.v_out = s.exp_avg_sq;
+        d.vmax_in = d.vmax_out = s.max_exp_avg_sq;
+        d.n = s.n;
+        int rc = check_update_tensor(d, gdt, amsgrad, first, true, dev, ranges);
+        if (rc) return rc;
+    }
+    if (active_out) *active_out = active;
+    return check_alias(ranges);
+}
+
+int64_t stats_rows(int64_t n, int gdt) {
+    if (n == 0) return 0;
+    const int64_t epc = gdt == RADAMW_F32 ? 4 : 8;
+    const int64_t per_row = int64_t(STATS_BLOCK) * STATS_UNROLL * epc;
+    return std::min<int64_t>((n + per_row - 1) / per_row, STATS_ROWS_CAP);
+}
+
+int32_t stats_head(const void *g, int gdt, int64_t n) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(g);
+    int64_t head = static_cast<int64_t>((16 - (a & 15)) & 15) / static_cast<int64_t>(grad_bytes(gdt));
+    return static_cast<int32_t>(std::min(head, n));
+}
+
+int plan(int64_t rows, int64_t *scratch_elements, int32_t *extra) {
+    if (rows < 1 || rows > STATS_MAX_ROWS) return RADAMW_ERR_RANGE;
+    int64_t remaining = rows, records = 0;
+    int32_t levels = 0;
+    while (remaining > MERGE_FAN_IN) {
+        remaining = (remaining + MERGE_FAN_IN - 1) / MERGE_FAN_IN;
+        records += remaining;
+        ++levels;
+    }
+    *scratch_elements = 3 * records;
+    *extra = levels;
+    return RADAMW_OK;
+}
+
+// Launch the merges for already validated arguments.
+int merge_launch(const StatsRec *rows, int64_t nrows, StatsRec *scratch, StatsRec *report,
+                 bool hierarchical, hipStream_t stream) {
+    const StatsRec *cur = rows;
+    int64_t count = nrows;
+    if (hierarchical) {
+        StatsRec *level = scratch;
+        while (count > MERGE_FAN_IN) {
+            const int64_t blocks = (count + MERGE_FAN_IN - 1) / MERGE_FAN_IN;
+            int rc = hip_status(launch_merge(cur, count, MERGE_FAN_IN, blocks, level, stream));
+            if (rc) return rc;
+            g_launches.fetch_add(1, std::memory_order_relaxed);
+            cur = level;
+            count = blocks;
+            level += blocks;
+        }
+    }
+    int rc = hip_status(launch_merge(cur, count, count, 1, report, stream));
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return RADAMW_OK;
+}
+
+int read_report(const StatsRec *report, radamw_stats *host, int dev, hipStream_t stream) {
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.mu);
+    if (!dc.pinned_report) {
+        void *p = nullptr;
+        hipError_t e = hipHostMalloc(&p, 64, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_status(e);
+        dc.pinned_report = static_cast<radamw_stats *>(p);
+    }
+    hipError_t e = hipMemcpyAsync(dc.pinned_report, report, sizeof(radamw_stats), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    std::memcpy(host, dc.pinned_report, sizeof(radamw_stats));
+    return RADAMW_OK;
+}
+
+void decode(const radamw_stats &r, double *sumsq, uint32_t *count) {
+    const uint64_t bits = uint64_t(r.w[0]) | (uint64_t(r.w[1]) << 32);
+    std::memcpy(sumsq, &bits, sizeof(double));
+    *count = r.w[2];
+}
+
+}  // namespace
+
+// ===================================================================== ABI ==
+
+extern "C" {
+
+radamw_options radamw_options_default(void) {
+    radamw_options o;
+    o.lr = 1e-3;
+    o.beta1 = 0.9;
+    o.beta2 = 0.999;
+    o.eps = 1e-5;
+    o.weight_decay = 1e-4;
+    o.amsgrad = 0;
+    o.maximize = 0;
+    return o;
+}
+
+int radamw_host_coefficients(const radamw_options *opts, uint64_t t, double gradient_scale,
+                             float *out9) {
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    if (!out9 || t == 0) return RADAMW_ERR_INVALID;
+    const Coefs c = make_coefs(*opts, t, gradient_scale);
+    const float v[9] = {c.beta1, c.one_minus_beta1, c.beta2, c.one_minus_beta2, c.inv_scale,
+                        c.decay, c.step_size, c.inv_bc2, c.eps};
+    std::memcpy(out9, v, sizeof v);
+    return RADAMW_OK;
+}
+
+int radamw_step(const float *p, const void *g, radamw_dtype gdt, int64_t n, const radamw_state *in,
+                float *p_out, radamw_state *out, const radamw_options *opts,
+                const radamw_control *ctrl, radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!valid_dtype(gdt) || n < 0 || !in || !out || !updated) return RADAMW_ERR_INVALID;
+    const bool ams = opts->amsgrad != 0;
+    const bool first = in->step == 0;
+    if (in->step == UINT64_MAX) return RADAMW_ERR_STATE;
+    if (n > 0) {
+        if ((out->max_exp_avg_sq != nullptr) != ams) return RADAMW_ERR_STATE;
+        if (!first && (in->max_exp_avg_sq != nullptr) != ams) return RADAMW_ERR_STATE;
+        int dev;
+        if ((rc = stream_device(stream, &dev))) return rc;
+        SegDesc d{};
+        d.p_in = p;
+        d.g = g;
+        d.m_in = in->exp_avg;
+        d.v_in = in->exp_avg_sq;
+        d.vmax_in = in->max_exp_avg_sq;
+        d.p_out = p_out;
+        d.m_out = out->exp_avg;
+        d.v_out = out->exp_avg_sq;
+        d.vmax_out = out->max_exp_avg_sq;
+        d.n = n;
+        std::vector<Range> ranges;
+        if ((rc = check_update_tensor(d, gdt, ams, first, false, dev, ranges))) return rc;
+        if ((rc = check_alias(ranges))) return rc;
+        if (ctrl->skip_update) {
+            *updated = 0;
+            return RADAMW_OK;
+        }
+        const Coefs c = make_coefs(*opts, in->step + 1, ctrl->gradient_scale);
+        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream))) return rc;
+        out->step = in->step + 1;
+        *updated = 1;
+        return RADAMW_OK;
+    }
+    *updated = 0;
+    return RADAMW_OK;
+}
+
+int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n, radamw_state *st,
+                        const radamw_options *opts, const radamw_control *ctrl,
+                        radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!valid_dtype(gdt) || n < 0 || !st || !updated) return RADAMW_ERR_INVALID;
+    if (st->step == UINT64_MAX) return RADAMW_ERR_STATE;
+    const bool ams = opts->amsgrad != 0;
+    if (n == 0) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    if ((st->max_exp_avg_sq != nullptr) != ams) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    radamw_segment s{p, g, st->exp_avg, st->exp_avg_sq, st->max_exp_avg_sq, n};
+    if ((rc = check_segments(&s, 1, gdt, ams, st->step == 0, dev, nullptr))) return rc;
+    if (ctrl->skip_update) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    return multi_update(&s, 1, gdt, &st->step, *opts, ctrl->gradient_scale, dev, stream, updated);
+}
+
+int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, uint64_t *step,
+                      const radamw_options *opts, const radamw_control *ctrl,
+                      radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!valid_dtype(gdt) || !step || !updated) return RADAMW_ERR_INVALID;
+    if (*step == UINT64_MAX) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    int64_t active = 0;
+    if ((rc = check_segments(segs, nseg, gdt, opts->amsgrad != 0, *step == 0, dev, &active))) return rc;
+    if (ctrl->skip_update || active == 0) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    return multi_update(segs, nseg, gdt, step, *opts, ctrl->gradient_scale, dev, stream, updated);
+}
+
+int radamw_stats_plan(int64_t rows, int64_t *scratch_elements, int32_t *extra_merge_kernels) {
+    if (!scratch_elements || !extra_merge_kernels) return RADAMW_ERR_INVALID;
+    int64_t se;
+    int32_t ex;
+    int rc = plan(rows, &se, &ex);
+    if (rc) return rc;
+    *scratch_elements = se;
+    *extra_merge_kernels = ex;
+    return RADAMW_OK;
+}
+
+int64_t radamw_grad_stats_rows(int64_t n, radamw_dtype gdt) {
+    if (n < 0 || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
+    return stats_rows(n, gdt);
+}
+
+int radamw_grad_stats(const void *g, radamw_dtype gdt, int64_t n, radamw_stats *rows_out,
+                      int64_t rows_capacity, int64_t *rows_written, radamw_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!valid_dtype(gdt) || n < 0 || !rows_written || rows_capacity < 0) return RADAMW_ERR_INVALID;
+    const int64_t rows = stats_rows(n, gdt);
+    if (rows == 0) {
+        *rows_written = 0;
+        return RADAMW_OK;
+    }
+    if (rows_capacity < rows) return RADAMW_ERR_RANGE;
+    int dev, rc;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    if ((rc = check_device_ptr(g, grad_bytes(gdt), dev))) return rc;
+    if ((rc = check_device_ptr(rows_out, 4, dev))) return rc;
+    std::vector<Range> ranges;
+    add_range(ranges, g, n * static_cast<int64_t>(grad_bytes(gdt)), false);
+    add_range(ranges, rows_out, rows * 12, true);
+    if ((rc = check_alias(ranges))) return rc;
+    rc = hip_status(launch_analyze(g, gdt, n, stats_head(g, gdt, n), rows,
+                                   reinterpret_cast<StatsRec *>(rows_out), stream));
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    *rows_written = rows;
+    return RADAMW_OK;
+}
+
+int radamw_merge_stats(const radamw_stats *rows, int64_t nrows, float *scratch,
+                       int64_t scratch_elements, radamw_stats *report, int32_t hierarchical,
+                       radamw_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (hierarchical != 0 && hierarchical != 1) return RADAMW_ERR_INVALID;
+    int64_t need;
+    int32_t extra;
+    int rc = plan(nrows, &need, &extra);
+    if (rc) return rc;
+    if (!hierarchical) need = 0;
+    if (scratch_elements < need || scratch_elements < 0) return RADAMW_ERR_RANGE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    if ((rc = check_device_ptr(rows, 4, dev))) return rc;
+    if ((rc = check_device_ptr(report, 4, dev))) return rc;
+    if (need > 0 && (rc = check_device_ptr(scratch, 4, dev))) return rc;
+    std::vector<Range> ranges;
+    add_range(ranges, rows, nrows * 12, false);
+    add_range(ranges, report, 12, true);
+    add_range(ranges, scratch, need * 4, true);
+    if ((rc = check_alias(ranges))) return rc;
+    return merge_launch(reinterpret_cast<const StatsRec *>(rows), nrows,
+                        reinterpret_cast<StatsRec *>(scratch), reinterpret_cast<StatsRec *>(report),
+                        hierarchical != 0, stream);
+}
+
+int radamw_read_report(const radamw_stats *report, radamw_stats *host_report, radamw_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!host_report) return RADAMW_ERR_INVALID;
+    int dev, rc;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    if ((rc = check_device_ptr(report, 4, dev))) return rc;
+    return read_report(reinterpret_cast<const StatsRec *>(report), host_report, dev, stream);
+}
+
+int radamw_decide(const radamw_stats *host_report, double gradient_scale, double max_grad_norm,
+                  radamw_control *ctrl, radamw_fused_result *result) {
+    if (!host_report || !ctrl || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    int rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    double sumsq;
+    uint32_t count;
+    decode(*host_report, &sumsq, &count);
+    const double norm = std::sqrt(sumsq) / gradient_scale;
+    double clip = 1.0;
+    if (max_grad_norm > 0.0) clip = std::min(1.0, max_grad_norm / (norm + 1e-6));
+    // a skipped step applies no clip: the scale passes through unchanged
+    ctrl->skip_update = count > 0 ? 1 : 0;
+    ctrl->gradient_scale = (count > 0 || clip == 1.0) ? gradient_scale : gradient_scale / clip;
+    if (result) {
+        result->found_inf = count > 0 ? 1 : 0;
+        result->nonfinite = count;
+        result->reserved = 0;
+        result->sumsq = sumsq;
+        result->total_norm = norm;
+        result->clip_coef = clip;
+    }
+    return RADAMW_OK;
+}
+
+int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt) {
+    if (nseg < 0 || (nseg > 0 && !segs) || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
+    int64_t rows = 0;
+    for (int32_t i = 0; i < nseg; ++i) {
+        if (segs[i].n < 0) return RADAMW_ERR_INVALID;
+        rows += stats_rows(segs[i].n, gdt);
+    }
+    if (rows == 0) return 0;
+    int64_t se;
+    int32_t ex;
+    int rc = plan(rows, &se, &ex);
+    if (rc) return rc;
+    return rows * 12 + se * 4 + 12;
+}
+
+int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt,
+                            uint64_t *step, const radamw_options *opts, double gradient_scale,
+                            double max_grad_norm, int32_t hierarchical, void *workspace,
+                            int64_t workspace_bytes, radamw_stream_t stream_,
+                            radamw_fused_result *result) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    if (!valid_dtype(gdt) || !step || !result || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    if (hierarchical != 0 && hierarchical != 1) return RADAMW_ERR_INVALID;
+    if (*step == UINT64_MAX) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    int64_t active = 0;
+    if ((rc = check_segments(segs, nseg, gdt, opts->amsgrad != 0, *step == 0, dev, &active))) return rc;
+    const int64_t need = radamw_fused_workspace_bytes(segs, nseg, gdt);
+    if (need < 0) return static_cast<int>(need);
+    std::memset(result, 0, sizeof *result);
+    result->clip_coef = 1.0;
+    if (active == 0) return RADAMW_OK;
+    if (workspace_bytes < need) return RADAMW_ERR_RANGE;
+    if ((rc = check_device_ptr(workspace, 4, dev))) return rc;
+    {
+        // the workspace is written; it may overlap no tensor of the step
+        std::vector<Range> ranges;
+        add_range(ranges, workspace, need, true);
+        for (int32_t i = 0; i < nseg; ++i) {
+            const radamw_segment &s = segs[i];
+            add_range(ranges, s.grad, s.n * static_cast<int64_t>(grad_bytes(gdt)), false);
+            add_range(ranges, s.param, s.n * 4, false);
+            add_range(ranges, s.exp_avg, s.n * 4, false);
+            add_range(ranges, s.exp_avg_sq, s.n * 4, false);
+            add_range(ranges, s.max_exp_avg_sq, s.n * 4, false);
+        }
+        if ((rc = check_alias(ranges))) return rc;
+    }
+
+    // statistics of every active gradient, rows packed back to back
+    StatsRec *rows = static_cast<StatsRec *>(workspace);
+    int64_t nrows = 0;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const radamw_segment &s = segs[i];
+        if (s.n == 0) continue;
+        const int64_t r = stats_rows(s.n, gdt);
+        rc = hip_status(launch_analyze(s.grad, gdt, s.n, stats_head(s.grad, gdt, s.n), r, rows + nrows, stream));
+        if (rc) return rc;
+        g_launches.fetch_add(1, std::memory_order_relaxed);
+        nrows += r;
+    }
+    int64_t se;
+    int32_t ex;
+    plan(nrows, &se, &ex);
+    StatsRec *scratch = rows + nrows;
+    StatsRec *report = scratch + se / 3;
+    if ((rc = merge_launch(rows, nrows, scratch, report, hierarchical != 0, stream))) return rc;
+
+    radamw_stats host;
+    if ((rc = read_report(report, &host, dev, stream))) return rc;
+    radamw_control ctrl;
+    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
+    if (ctrl.skip_update) {
+        result->updated = 0;
+        return RADAMW_OK;
+    }
+    int32_t updated = 0;
+    rc = multi_update(segs, nseg, gdt, step, *opts, ctrl.gradient_scale, dev, stream, &updated);
+    if (rc) return rc;
+    result->updated = updated;
+    return RADAMW_OK;
+}
+
+const char *radamw_status_string(int status) {
+    switch (status) {
+    case RADAMW_OK: return "ok (submitted)";
+    case RADAMW_ERR_INVALID: return "invalid argument";
+    case RADAMW_ERR_STATE: return "optimizer state mismatch";
+    case RADAMW_ERR_ALIAS: return "overlapping buffers";
+    case RADAMW_ERR_ALIGN: return "misaligned pointer";
+    case RADAMW_ERR_RANGE: return "size or capacity out of range";
+    case RADAMW_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int radamw_last_hip_error(void) { return g_last_hip; }
+
+uint64_t radamw_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// radamw_internal.h -- structures shared by the C-ABI layer (radamw_api.cpp)
+// and the gfx950 kernels (radamw_update.hip, radamw_stats.hip).  Not part of
+// the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace radamw {
+
+// Workgroup shape of the update kernels: 256 lanes = 4 wave64s.  Each lane
+// owns UPDATE_UNROLL 16-byte FP32 chunks (4 elements each) per tile.
+constexpr int UPDATE_BLOCK = 256;
+#ifndef RADAMW_UPDATE_UNROLL
+#define RADAMW_UPDATE_UNROLL 4
+#endif
+constexpr int UPDATE_UNROLL = RADAMW_UPDATE_UNROLL;
+constexpr int64_t UPDATE_TILE_CHUNKS = int64_t(UPDATE_BLOCK) * UPDATE_UNROLL;  // float4 chunks per tile
+constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
+
+// Grid cap of the update kernels, in workgroups per compute unit; the kernels
+// stride over tiles when there are more tiles than workgroups.
+#ifndef RADAMW_UPDATE_BLOCKS_PER_CU
+#define RADAMW_UPDATE_BLOCKS_PER_CU 8
+#endif
+
+// Statistics: 256-lane analysis workgroups, each lane loads STATS_UNROLL
+// 16-byte chunks per pass; one record ("row") per workgroup.
+constexpr int STATS_BLOCK = 256;
+constexpr int STATS_UNROLL = 4;
+constexpr int64_t STATS_ROWS_CAP = 2048;     // records per analysis launch, at most
+constexpr int MERGE_BLOCK = 1024;            // merge workgroup = fan-in
+constexpr int64_t MERGE_FAN_IN = 1024;
+constexpr int64_t STATS_MAX_ROWS = 4194304;  // accepted by the merge plan
+
+enum GradType : int { G_F32 = 0, G_F16 = 1, G_BF16 = 2 };
+
+// FP32 coefficients of one update, formed on the host in FP64 and cast.
+struct Coefs {
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float inv_scale;   // +-1 / gradient_scale (sign carries maximize)
+    float decay;       // 1 - lr * weight_decay
+    float step_size;   // lr / (1 - beta1^t)
+    float inv_bc2;     // 1 / (1 - beta2^t)
+    float eps;
+};
+
+// One contiguous tensor as the kernels see it.  For an in-place update the
+// *_out pointers equal the *_in pointers.  head is the number of leading
+// elements handled by scalar code so that every stream is 16-byte aligned
+// from element `head` on (0..3); head == -1 marks a segment whose streams
+// are not mutually aligned, processed entirely by scalar code.
+struct SegDesc {
+    const float *p_in;
+    const void *g;
+    const float *m_in;
+    const float *v_in;
+    const float *vmax_in;
+    float *p_out;
+    float *m_out;
+    float *v_out;
+    float *vmax_out;
+    int64_t n;
+    int64_t tile_begin;  // first tile of this segment in the launch's tile space
+    int32_t head;
+    int32_t pad;
+};
+
+// Tiles a segment occupies (0 for an empty segment).
+__host__ __device__ inline int64_t segment_tiles(int64_t n, int32_t head) {
+    if (n == 0) return 0;
+    if (head < 0) return (n + UPDATE_TILE_ELEMS - 1) / UPDATE_TILE_ELEMS;
+    int64_t body_chunks = (n - head) / 4;
+    int64_t t = (body_chunks + UPDATE_TILE_CHUNKS - 1) / UPDATE_TILE_CHUNKS;
+    return t < 1 ? 1 : t;
+}
+
+// 12-byte statistics record: w[0] | w[1] << 32 = binary64 sum of squares of
+// finite values, w[2] = saturating non-finite count.
+struct StatsRec {
+    uint32_t w[3];
+};
+
+// Launchers (host functions defined next to the kernels).  They return the
+// hipError_t of the launch.
+hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
+                                bool first, int grid, hipStream_t stream);
+hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
+                               int32_t nseg, int64_t total_tiles, const Coefs &c, int gdt,
+                               bool amsgrad, bool first, int grid, hipStream_t stream);
+hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
+                          StatsRec *out, hipStream_t stream);
+hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
+                        StatsRec *out, hipStream_t stream);
+
+}  // namespace radamw

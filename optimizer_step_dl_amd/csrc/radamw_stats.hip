@@ -1,0 +1,189 @@
+// radamw_stats.hip -- gradient statistics for gfx950: the read-only analysis
+// pass and the fan-in-1024 merge.
+//
+// Page abbreviations: FA-ja = RUDA docs page "実験的なデバイス上の融合 AdamW /
+// AMSGrad"; TR-zh = "训练与状态保存".
+//
+// The analysis pass (FA-ja "ネイティブ PyTorch ストレージと階層統計":
+// analyze_gradient) reads a gradient once and writes one 12-byte record per
+// workgroup: the FP64 sum of squares of the finite values and the count of
+// non-finite ones.  The merges (merge_gradient_stats_chunks /
+// merge_gradient_stats) reduce up to 1024 records per workgroup; a
+// 1024-lane workgroup gives each lane one record, so fan-in equals the
+// workgroup size (TR-zh "在 ruda:0 上进行原生 PyTorch 训练": fan-in 1024).
+//
+// No atomics anywhere: every lane accumulates a fixed set of elements in a
+// fixed order, wave64 butterflies (__shfl_xor) and a fixed LDS pass finish
+// the workgroup, so the same input gives the same bits on every run.
+#include "radamw_internal.h"
+
+namespace radamw {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Acc {
+    double s[4];
+    uint32_t bad;
+};
+
+__device__ __forceinline__ void acc_value(Acc &a, int slot, float x) {
+    const bool finite = __builtin_isfinite(x);
+    const double d = finite ? static_cast<double>(x) : 0.0;
+    a.s[slot] = __builtin_fma(d, d, a.s[slot]);  // d*d is exact in binary64
+    a.bad += finite ? 0u : 1u;
+}
+
+template <int GDT>
+__device__ __forceinline__ void acc_chunk(Acc &a, const void *g, int64_t chunk) {
+    if constexpr (GDT == G_F32) {
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(g) + chunk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc_value(a, j, x[j]);
+    } else if constexpr (GDT == G_F16) {
+        const f16x8 h = __builtin_nontemporal_load(reinterpret_cast<const f16x8 *>(g) + chunk);
+        const f32x8 x = __builtin_convertvector(h, f32x8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc_value(a, j & 3, x[j]);
+    } else {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(g) + chunk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc_value(a, j, __builtin_bit_cast(float, w[j] << 16));
+            acc_value(a, j, __builtin_bit_cast(float, w[j] & 0xffff0000u));
+        }
+    }
+}
+
+template <int GDT>
+__device__ __forceinline__ float load_one(const void *g, int64_t e) {
+    if constexpr (GDT == G_F32) return static_cast<const float *>(g)[e];
+    else if constexpr (GDT == G_F16) return static_cast<float>(static_cast<const _Float16 *>(g)[e]);
+    else return __builtin_bit_cast(float, uint32_t(static_cast<const uint16_t *>(g)[e]) << 16);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ void write_record(StatsRec *out, double s, uint64_t count) {
+    const uint64_t bits = __builtin_bit_cast(uint64_t, s);
+    out->w[0] = uint32_t(bits);
+    out->w[1] = uint32_t(bits >> 32);
+    out->w[2] = count > 0xffffffffull ? 0xffffffffu : uint32_t(count);
+}
+
+// Fixed-order workgroup reduction; lane 0 writes the record.
+template <int BLOCK>
+__device__ __forceinline__ void block_finish(double s, uint64_t count, StatsRec *out) {
+    constexpr int WAVES = BLOCK / 64;
+    __shared__ double ws[WAVES];
+    __shared__ uint64_t wc[WAVES];
+    s = wave_sum(s);
+    count = wave_sum(count);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        ws[wave] = s;
+        wc[wave] = count;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double total = 0.0;
+        uint64_t c = 0;
+        for (int w = 0; w < WAVES; ++w) {
+            total += ws[w];
+            c += wc[w];
+        }
+        write_record(out, total, c);
+    }
+}
+
+// Elements [0, head) and the tail after the last whole 16-byte chunk are
+// scalar (workgroup 0); the body is walked in passes of STATS_BLOCK *
+// STATS_UNROLL chunks, workgroup b taking passes b, b + rows, b + 2 rows ...
+template <int GDT>
+__global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64_t n, int32_t head,
+                                                            int64_t rows, StatsRec *out) {
+    constexpr int EPC = GDT == G_F32 ? 4 : 8;  // elements per 16-byte chunk
+    constexpr int64_t PASS = int64_t(STATS_BLOCK) * STATS_UNROLL;
+    const int tid = threadIdx.x;
+    const int64_t body = (n - head) / EPC;
+    const void *gb = static_cast<const char *>(g) + int64_t(head) * (GDT == G_F32 ? 4 : 2);
+
+    Acc a;
+    a.s[0] = a.s[1] = a.s[2] = a.s[3] = 0.0;
+    a.bad = 0;
+    for (int64_t base = int64_t(blockIdx.x) * PASS; base < body; base += rows * PASS) {
+        if (base + PASS <= body) {
+#pragma unroll
+            for (int u = 0; u < STATS_UNROLL; ++u) acc_chunk<GDT>(a, gb, base + u * STATS_BLOCK + tid);
+        } else {
+#pragma unroll
+            for (int u = 0; u < STATS_UNROLL; ++u) {
+                const int64_t k = base + u * STATS_BLOCK + tid;
+                if (k < body) acc_chunk<GDT>(a, gb, k);
+            }
+        }
+    }
+    if (blockIdx.x == 0) {
+        const int64_t tail = n - head - body * EPC;
+        if (tid < head + tail) {
+            const int64_t e = tid < head ? int64_t(tid) : head + body * EPC + (tid - head);
+            acc_value(a, 0, load_one<GDT>(g, e));
+        }
+    }
+    const double s = (a.s[0] + a.s[1]) + (a.s[2] + a.s[3]);
+    block_finish<STATS_BLOCK>(s, a.bad, out + blockIdx.x);
+}
+
+// Workgroup b reduces records [b * per_block, min(nin, (b + 1) * per_block)).
+__global__ __launch_bounds__(MERGE_BLOCK) void stats_merge(const StatsRec *in, int64_t nin,
+                                                           int64_t per_block, StatsRec *out) {
+    const int64_t begin = int64_t(blockIdx.x) * per_block;
+    int64_t end = begin + per_block;
+    if (end > nin) end = nin;
+    double s = 0.0;
+    uint64_t c = 0;
+    for (int64_t r = begin + threadIdx.x; r < end; r += MERGE_BLOCK) {
+        const StatsRec rec = in[r];
+        s += __builtin_bit_cast(double, uint64_t(rec.w[0]) | (uint64_t(rec.w[1]) << 32));
+        c += rec.w[2];
+    }
+    block_finish<MERGE_BLOCK>(s, c, out + blockIdx.x);
+}
+
+hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
+                          StatsRec *out, hipStream_t stream) {
+    switch (gdt) {
+    case G_F32:
+        hipLaunchKernelGGL(grad_analyze<G_F32>, dim3(rows), dim3(STATS_BLOCK), 0, stream, g, n, head, rows, out);
+        break;
+    case G_F16:
+        hipLaunchKernelGGL(grad_analyze<G_F16>, dim3(rows), dim3(STATS_BLOCK), 0, stream, g, n, head, rows, out);
+        break;
+    case G_BF16:
+        hipLaunchKernelGGL(grad_analyze<G_BF16>, dim3(rows), dim3(STATS_BLOCK), 0, stream, g, n, head, rows, out);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
+                        StatsRec *out, hipStream_t stream) {
+    hipLaunchKernelGGL(stats_merge, dim3(nblocks), dim3(MERGE_BLOCK), 0, stream, in, nin, per_block, out);
+    return hipGetLastError();
+}
+
+}  // namespace radamw

@@ -1,0 +1,174 @@
+"""GPU parity of the gradient statistics (radamw_grad_stats, radamw_merge_stats,
+radamw_read_report) and of the fused step (radamw_fused_step_multi) against the
+CPU oracle.  Counts and skip decisions are compared exactly; sums of squares
+against math.fsum-exact values within FP64 rounding.
+
+Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGrad",
+TR-zh = "训练与状态保存"."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import optimizer_step_dl_amd as ra
+from gpu_helpers import DEV, TORCH_GDT, announce, contract_one_step, grad_host, host, new_gpu_state, oracle_opts
+
+pytestmark = pytest.mark.gpu
+
+
+def _inject(g: torch.Tensor, k: int, key) -> np.ndarray:
+    pos = synth.nonfinite_positions(g.numel(), k, key)
+    vals = torch.tensor(synth.nonfinite_values(k), dtype=g.dtype, device=g.device)
+    g[torch.from_numpy(pos).to(g.device)] = vals
+    return pos
+
+
+def _exact_sumsq(g_host: np.ndarray, gdt: str) -> float:
+    x = oracle.widen(g_host, gdt).astype(np.float64) if g_host.size < 300000 else None
+    if x is None:
+        t = torch.from_numpy(g_host.view(np.int16) if gdt != "f32" else g_host)
+        if gdt != "f32":
+            t = t.view(TORCH_GDT[gdt])
+        x = t.double().numpy()
+    x = x[np.isfinite(x)]
+    return math.fsum((x * x).tolist())
+
+
+def _stats_gpu(grads, hierarchical=True):
+    rows_total = sum(ra.radamw_grad_stats_rows(g.numel(), g.dtype) for g in grads)
+    rows = torch.zeros(3 * max(rows_total, 1), dtype=torch.int32, device=DEV)
+    off = 0
+    for g in grads:
+        off += ra.radamw_grad_stats(g, rows, off)
+    assert off == rows_total
+    se, _ = ra.radamw_stats_plan(rows_total)
+    scratch = torch.zeros(max(se, 1), dtype=torch.float32, device=DEV)
+    report = torch.zeros(3, dtype=torch.int32, device=DEV)
+    ra.radamw_merge_stats(rows, rows_total, scratch if se else None, report, hierarchical)
+    rep = ra.radamw_read_report(report)
+    return rep.sumsq, rep.nonfinite, rows_total
+
+
+@pytest.mark.parametrize("gdt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 4096, 8193, 100003, 3_000_001])
+def test_grad_stats_single_tensor(gdt, n):
+    announce(f"stats {gdt} n={n}")
+    g = synth.stored_grad(n, 1e-2, 64.0, gdt, (0, "st", gdt, n)).to(DEV)
+    k = min(n // 3, 11)
+    if k:
+        _inject(g, k, (0, "st", gdt, n, "pos"))
+    gh = grad_host(g)
+    s_ref, c_ref = oracle.grad_stats(gh, gdt)
+    s_gpu, c_gpu, _ = _stats_gpu([g])
+    assert c_gpu == c_ref == k
+    exact = _exact_sumsq(gh, gdt)
+    assert abs(s_gpu - exact) <= 1e-12 * exact and abs(s_ref - exact) <= 1e-12 * exact
+
+
+def test_grad_stats_list_hierarchical_vs_flat_and_deterministic():
+    announce("stats list hierarchical/flat")
+    sizes = [5, 4096, 2047, 2049, 9_000_001, 17, 4_000_000, 640_001]
+    grads = [synth.stored_grad(n, 1e-4, 1.0, "bf16", (0, "sl", i)).to(DEV) for i, n in enumerate(sizes)]
+    _inject(grads[4], 5, (0, "sl", "pos"))
+    acc = oracle.StatsAccumulator()
+    for g in grads:
+        acc.add(grad_host(g), "bf16")
+    s_ref, c_ref = acc.result
+    s_h, c_h, rows = _stats_gpu(grads, True)
+    s_f, c_f, _ = _stats_gpu(grads, False)
+    s_h2, c_h2, _ = _stats_gpu(grads, True)
+    assert rows > 1024  # at least one intermediate merge level
+    assert c_h == c_f == c_ref == 5
+    assert s_h == s_h2 and c_h2 == c_h  # bit-identical repeat
+    assert abs(s_h - s_ref) <= 2e-12 * s_ref and abs(s_f - s_ref) <= 2e-12 * s_ref
+
+
+@pytest.mark.parametrize("nrows", [1, 1024, 1025, 1048576, 1048577, 4194304])
+def test_merge_levels_on_synthetic_rows(nrows):
+    """Rows with dyadic sums and known counts: the merged report is exact."""
+    announce(f"merge rows={nrows}")
+    r = torch.arange(nrows, device=DEV, dtype=torch.int64)
+    vals = ((r % 7) + 1).double() * 0.25          # dyadic: every partial sum exact
+    bits = vals.view(torch.int64)
+    rows = torch.stack([(bits & 0xFFFFFFFF).to(torch.int64), (bits >> 32) & 0xFFFFFFFF, r % 3], dim=1)
+    rows = rows.to(torch.int32).contiguous().view(-1)
+    se, extra = ra.radamw_stats_plan(nrows)
+    scratch = torch.zeros(max(se, 1), dtype=torch.float32, device=DEV)
+    report = torch.zeros(3, dtype=torch.int32, device=DEV)
+    before = ra.radamw_launch_count()
+    ra.radamw_merge_stats(rows, nrows, scratch if se else None, report, True)
+    assert ra.radamw_launch_count() == before + extra + 1
+    rep = ra.radamw_read_report(report)
+    assert rep.sumsq == float(vals.sum().item())
+    assert rep.nonfinite == int((r % 3).sum().item())
+
+
+def test_merge_count_saturates():
+    nrows = 3000
+    rows = torch.zeros(nrows, 3, dtype=torch.int64)
+    rows[:, 2] = 0xFFFFFFF0
+    rows = rows.to(torch.int32).view(-1).to(DEV)  # wraps to the same bit pattern
+    report = torch.zeros(3, dtype=torch.int32, device=DEV)
+    scratch = torch.zeros(ra.radamw_stats_plan(nrows)[0], device=DEV)
+    ra.radamw_merge_stats(rows, nrows, scratch, report, True)
+    assert ra.radamw_read_report(report).nonfinite == 2**32 - 1
+
+
+def _fused_case(sizes, gdt, inject, max_norm, key, step0=0, amsgrad=False, hierarchical=True):
+    opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
+    scale = 1.0
+    segs, refs = [], []
+    for i, n in enumerate(sizes):
+        p0 = synth.normal(n, 0.02, key + (i, "p"))
+        g = synth.stored_grad(n, 1e-4, 1.0, gdt, key + (i, "g")).to(DEV)
+        st = new_gpu_state(n, amsgrad)
+        segs.append(ra.Segment(p0.to(DEV), g, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq))
+        refs.append((p0.numpy().copy(), oracle.State(n, amsgrad)))
+    if inject:
+        _inject(segs[len(segs) // 2].grad, inject, key + ("pos",))
+    acc = oracle.StatsAccumulator()
+    for s in segs:
+        acc.add(grad_host(s.grad), gdt)
+    s_ref, c_ref = acc.result
+    skip_ref, eff_ref = oracle.decide(s_ref, c_ref, scale, max_norm)
+    ws = torch.zeros(ra.radamw_fused_workspace_bytes(segs), dtype=torch.uint8, device=DEV)
+    before = ra.radamw_launch_count()
+    snap = [s.param.clone() for s in segs]
+    res, step = ra.radamw_fused_step_multi(segs, step0, opts, scale, max_norm, hierarchical, ws)
+    torch.cuda.synchronize()
+    assert res.nonfinite == c_ref and bool(res.found_inf) == skip_ref
+    assert abs(res.sumsq - s_ref) <= 2e-12 * max(s_ref, 1e-300)
+    launched = ra.radamw_launch_count() - before
+    nstats = len([n for n in sizes if n])
+    if skip_ref:
+        assert not res.updated and step == step0
+        assert all(torch.equal(a, s.param) for a, s in zip(snap, segs))
+        assert launched == nstats + 1 + ra.radamw_stats_plan(sum(ra.radamw_grad_stats_rows(n, TORCH_GDT[gdt]) for n in sizes))[1]
+    else:
+        assert res.updated and step == step0 + 1
+        for (p_ref, st_ref), s in zip(refs, segs):
+            oracle.adamw_step(p_ref, grad_host(s.grad), gdt, st_ref, oracle_opts(opts), eff_ref)
+            contract_one_step(host(s.param), p_ref, "fused p")
+            contract_one_step(host(s.exp_avg), st_ref.exp_avg, "fused m")
+    return res
+
+
+def test_fused_step_clips_when_norm_exceeds_max():
+    announce("fused clip")
+    res = _fused_case([4096, 1_000_000, 2049, 300_000], "bf16", 0, 0.05, (0, "fc"))
+    assert res.clip_coef < 1.0 and res.total_norm > 0.05
+
+
+def test_fused_step_without_clip_is_plain_update():
+    announce("fused no clip")
+    res = _fused_case([4096, 50_000], "f32", 0, 1e6, (0, "fn"))
+    assert res.clip_coef == 1.0
+
+
+def test_fused_step_found_inf_skips_everything():
+    announce("fused found_inf")
+    res = _fused_case([4096, 1_000_000, 2049], "bf16", 3, 1.0, (0, "fi"), step0=4)
+    assert res.found_inf and res.nonfinite == 3

@@ -1,0 +1,385 @@
+"""GPU parity of the fused update (radamw_step / _inplace / _multi) against
+the CPU oracle on the same seeded inputs, element by element.
+
+Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGrad",
+FA-zh = "实验性融合 AdamW / AMSGrad"."""
+import ctypes
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import optimizer_step_dl_amd as ra
+from optimizer_step_dl_amd import _abi
+from gpu_helpers import (DEV, TORCH_GDT, announce, bits_equal, contract_one_step, grad_host, host,
+                         new_gpu_state, normwise, oracle_opts, snapshot, ulps_of, unchanged)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_state_from(n, amsgrad):
+    return oracle.State(n, amsgrad)
+
+
+def _compare_state(p_gpu, st_gpu, p_ref, st_ref, amsgrad, what, one_step):
+    check = contract_one_step if one_step else normwise
+    check(host(p_gpu), p_ref, f"{what} p")
+    check(host(st_gpu.exp_avg), st_ref.exp_avg, f"{what} m")
+    check(host(st_gpu.exp_avg_sq), st_ref.exp_avg_sq, f"{what} v")
+    if amsgrad:
+        check(host(st_gpu.max_exp_avg_sq), st_ref.max_exp_avg_sq, f"{what} vmax")
+    assert st_gpu.step == st_ref.step
+
+
+# ------------------------------------------------------------- config 1 --
+
+def test_fp32_adamw_ten_fresh_steps_65536():
+    """65,536 FP32 params N(0,0.02), FP32 grads N(0,1e-3) fresh each step,
+    zero state, AdamW defaults, scale 1, 10 steps; in place and out of place."""
+    n = 65536
+    announce("fp32 adamw 65536 x10")
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    p0 = synth.normal(n, 0.02, (0, "cfg1", "p"))
+    grads = [synth.stored_grad(n, 1e-3, 1.0, "f32", (0, "cfg1", "g", t)) for t in range(10)]
+
+    p_ip = p0.to(DEV)
+    st_ip = new_gpu_state(n, False)
+    # out of place: ping-pong between two caller-owned buffer sets
+    bufs = [(p0.to(DEV), new_gpu_state(n, False)), (torch.empty_like(p_ip), new_gpu_state(n, False))]
+    cur = 0
+    p_ref, st_ref = p0.numpy().copy(), oracle.State(n, False)
+    m_scale = np.zeros(n)
+    for t, g in enumerate(grads, start=1):
+        gd = g.to(DEV)
+        assert ra.radamw_step_inplace(p_ip, gd, st_ip, opts, ra.control(1.0))
+        src_p, src_s = bufs[cur]
+        dst_p, dst_s = bufs[1 - cur]
+        assert ra.radamw_step(src_p, gd, src_s, opts, ra.control(1.0), dst_p, dst_s)
+        cur = 1 - cur
+        oracle.adamw_step(p_ref, grad_host(g), "f32", st_ref, oracle_opts(opts), 1.0)
+        m_scale = 0.9 * m_scale + 0.1 * np.abs(g.numpy().astype(np.float64))
+        torch.cuda.synchronize()
+        _compare_state(p_ip, st_ip, p_ref, st_ref, False, f"step {t}", one_step=True)
+        ulps_of(host(st_ip.exp_avg), st_ref.exp_avg, m_scale.astype(np.float32), 4 * t, f"m step {t}")
+        ulps_of(host(st_ip.exp_avg_sq), st_ref.exp_avg_sq, st_ref.exp_avg_sq, 8 * t, f"v step {t}")
+        # the out-of-place path runs the same arithmetic: bit-identical
+        op_p, op_s = bufs[cur]
+        assert op_s.step == t
+        assert bits_equal(op_p, p_ip) and bits_equal(op_s.exp_avg, st_ip.exp_avg)
+        assert bits_equal(op_s.exp_avg_sq, st_ip.exp_avg_sq)
+
+
+# ------------------------------------------------------------- config 2 --
+
+@pytest.mark.parametrize("n", [65536, 65537])
+def test_bf16_amsgrad_hundred_calls_with_skips(n):
+    """BF16 grads stored as N(0,1e-3)*128 with scale 128, AMSGrad, lr 1e-3,
+    wd 0.01, 100 calls from zero state, skip_update on calls 37 and 38."""
+    announce(f"bf16 amsgrad {n} x100")
+    opts = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=True)
+    p0 = synth.normal(n, 0.02, (0, "cfg2", n, "p"))
+    p = p0.to(DEV)
+    st = new_gpu_state(n, True)
+    p_ref, st_ref = p0.numpy().copy(), oracle.State(n, True)
+    oo = oracle_opts(opts)
+    for call in range(1, 101):
+        g = synth.stored_grad(n, 1e-3, 128.0, "bf16", (0, "cfg2", n, "g", call))
+        skip = call in (37, 38)
+        gd = g.to(DEV)
+        if skip:
+            torch.cuda.synchronize()
+            before = snapshot(p, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq)
+            launches, step = ra.radamw_launch_count(), st.step
+        ran = ra.radamw_step_inplace(p, gd, st, opts, ra.control(128.0, skip))
+        ran_ref = oracle.adamw_step(p_ref, grad_host(g), "bf16", st_ref, oo, 128.0, skip)
+        assert ran == ran_ref == (not skip)
+        if skip:
+            torch.cuda.synchronize()
+            assert ra.radamw_launch_count() == launches and st.step == step
+            assert unchanged(before, [p, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq])
+        if call == 1:
+            torch.cuda.synchronize()
+            _compare_state(p, st, p_ref, st_ref, True, "call 1", one_step=True)
+            # first AMSGrad step: v_max is v itself
+            assert bits_equal(st.max_exp_avg_sq, st.exp_avg_sq)
+    torch.cuda.synchronize()
+    assert st.step == st_ref.step == 98
+    _compare_state(p, st, p_ref, st_ref, True, "after 100 calls", one_step=False)
+    contract_one_step(host(p), p_ref, "p after 100 calls (per element)")
+    vmax, v = host(st.max_exp_avg_sq), host(st.exp_avg_sq)
+    assert np.all(vmax >= v)
+
+
+# ------------------------------------------------------ 12-case matrix --
+
+MATRIX = list(itertools.product(["f32", "f16", "bf16"], [False, True], [False, True]))
+
+
+@pytest.mark.parametrize("gdt,amsgrad,maximize", MATRIX)
+def test_matrix_five_steps_several_tiles(gdt, amsgrad, maximize):
+    """3 grad dtypes x AMSGrad x maximize, 5 steps, a size spanning several
+    4096-element tiles with a ragged tail; options where every term of the
+    formula is visible; a non-power-of-two scale."""
+    n = 3 * 4096 + 1031
+    announce(f"matrix {gdt} ams={amsgrad} max={maximize}")
+    opts = ra.options(lr=1e-2, beta1=0.8, beta2=0.95, eps=1e-3, weight_decay=0.1, amsgrad=amsgrad,
+                      maximize=maximize)
+    scale = 1000.0
+    p0 = synth.normal(n, 0.02, (0, "mx", gdt, "p"))
+    p, st = p0.to(DEV), new_gpu_state(n, amsgrad)
+    p_ref, st_ref = p0.numpy().copy(), oracle.State(n, amsgrad)
+    for t in range(1, 6):
+        g = synth.stored_grad(n, 1e-3 if t % 2 else 3e-2, scale, gdt, (0, "mx", gdt, "g", t))
+        assert ra.radamw_step_inplace(p, g.to(DEV), st, opts, ra.control(scale))
+        oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts), scale)
+        torch.cuda.synchronize()
+        _compare_state(p, st, p_ref, st_ref, amsgrad, f"t={t}", one_step=True)
+
+
+# ------------------------------------------------------------ tails --
+
+TAIL_SIZES = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
+              4095, 4096, 4097, 8191, 8193, 65537]
+
+
+@pytest.mark.parametrize("gdt,amsgrad", [("f32", False), ("bf16", True), ("f16", False)])
+def test_tail_lengths(gdt, amsgrad):
+    announce(f"tails {gdt} ams={amsgrad}")
+    opts = ra.options(lr=1e-2, weight_decay=0.1, amsgrad=amsgrad)
+    for n in TAIL_SIZES:
+        p0 = synth.normal(n, 0.02, (0, "tail", n, "p"))
+        p, st = p0.to(DEV), new_gpu_state(n, amsgrad)
+        p_ref, st_ref = p0.numpy().copy(), oracle.State(n, amsgrad)
+        for t in (1, 2):
+            g = synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "tail", n, "g", t))
+            ra.radamw_step_inplace(p, g.to(DEV), st, opts, ra.control())
+            oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts))
+        torch.cuda.synchronize()
+        _compare_state(p, st, p_ref, st_ref, amsgrad, f"n={n}", one_step=True)
+
+
+@pytest.mark.parametrize("phases", [(1, 1, 1, 1, 1), (3, 3, 3, 3, 3), (1, 2, 1, 1, 3), (0, 0, 0, 2, 0)])
+def test_views_at_offsets(phases):
+    """Views starting at element offsets: equal offsets take the aligned
+    vector body after a scalar head; unequal offsets take the scalar path."""
+    n = 10000
+    announce(f"offset views {phases}")
+    gdt = "bf16"
+    opts = ra.options(lr=1e-2, weight_decay=0.1, amsgrad=True)
+    op, og, om, ov, ox = phases
+    P = torch.zeros(n + 4, device=DEV)
+    G = torch.zeros(n + 4, device=DEV, dtype=torch.bfloat16)
+    M, V, X = (torch.zeros(n + 4, device=DEV) for _ in range(3))
+    p0 = synth.normal(n, 0.02, (0, "off", "p"))
+    p, m, v, x = P[op:op + n], M[om:om + n], V[ov:ov + n], X[ox:ox + n]
+    p.copy_(p0.to(DEV))
+    st = ra.AdamWState(0, m, v, x)
+    p_ref, st_ref = p0.numpy().copy(), oracle.State(n, True)
+    for t in (1, 2, 3):
+        g = synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "off", "g", t))
+        G[og:og + n].copy_(g.to(DEV))
+        ra.radamw_step_inplace(p, G[og:og + n], st, opts, ra.control())
+        oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts))
+    torch.cuda.synchronize()
+    _compare_state(p, st, p_ref, st_ref, True, f"phases {phases}", one_step=True)
+    # nothing outside the views was written
+    for buf, off in ((P, op), (M, om), (V, ov), (X, ox)):
+        outside = torch.cat([buf[:off], buf[off + n:]])
+        assert not torch.any(outside != 0)
+
+
+# ------------------------------------------------------------ multi --
+
+def _make_segments(sizes, gdt, amsgrad, key):
+    segs, refs = [], []
+    for i, n in enumerate(sizes):
+        p0 = synth.normal(n, 0.02, key + (i, "p"))
+        st = new_gpu_state(n, amsgrad)
+        segs.append(ra.Segment(p0.to(DEV), torch.empty(n, device=DEV, dtype=TORCH_GDT[gdt]), st.exp_avg,
+                               st.exp_avg_sq, st.max_exp_avg_sq))
+        refs.append((p0.numpy().copy(), oracle.State(n, amsgrad)))
+    return segs, refs
+
+
+@pytest.mark.parametrize("gdt,amsgrad", [("f16", True), ("f32", False)])
+def test_multi_tensor_one_launch_matches_oracle_and_per_tensor(gdt, amsgrad):
+    sizes = [0, 1, 5, 4096, 4097, 2047, 2049, 100000, 0, 3, 70001, 2048]
+    announce(f"multi {gdt} ams={amsgrad}")
+    opts = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=amsgrad)
+    scale = 1024.0
+    segs, refs = _make_segments(sizes, gdt, amsgrad, (0, "multi", gdt))
+    twins, _ = _make_segments(sizes, gdt, amsgrad, (0, "multi", gdt))  # per-tensor launches
+    twin_states = [ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq) for s in twins]
+    step = 0
+    for t in range(1, 4):
+        for i, (s, tw) in enumerate(zip(segs, twins)):
+            g = synth.stored_grad(sizes[i], 1e-4, scale, gdt, (0, "multi", gdt, i, "g", t))
+            s.grad.copy_(g.to(DEV))
+            tw.grad.copy_(s.grad)
+            oracle.adamw_step(refs[i][0], grad_host(g), gdt, refs[i][1], oracle_opts(opts), scale)
+        before = ra.radamw_launch_count()
+        updated, step = ra.radamw_step_multi(segs, step, opts, ra.control(scale))
+        assert updated and step == t
+        assert ra.radamw_launch_count() == before + 1
+        for tw, ts in zip(twins, twin_states):
+            ra.radamw_step_inplace(tw.param, tw.grad, ts, opts, ra.control(scale))
+    torch.cuda.synchronize()
+    for i, (s, tw) in enumerate(zip(segs, twins)):
+        if sizes[i] == 0:
+            continue  # an empty tensor has nothing to compare (its oracle state never steps)
+        st = ra.AdamWState(step, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)
+        _compare_state(s.param, st, refs[i][0], refs[i][1], amsgrad, f"segment {i} n={sizes[i]}", True)
+        assert bits_equal(s.param, tw.param) and bits_equal(s.exp_avg_sq, tw.exp_avg_sq)
+
+
+def test_multi_all_empty_launches_nothing():
+    segs = [ra.Segment(torch.empty(0, device=DEV), torch.empty(0, device=DEV), torch.empty(0, device=DEV),
+                       torch.empty(0, device=DEV))] * 3
+    before = ra.radamw_launch_count()
+    updated, step = ra.radamw_step_multi(segs, 5, ra.options(), ra.control())
+    assert not updated and step == 5 and ra.radamw_launch_count() == before
+    updated, step = ra.radamw_step_multi([], 5, ra.options(), ra.control())
+    assert not updated and step == 5
+
+
+# ------------------------------------------------------- skip / resume --
+
+def test_skip_and_empty_launch_nothing_and_write_nothing():
+    n = 5000
+    opts = ra.options(amsgrad=True)
+    p = synth.normal(n, 0.02, (0, "skip", "p")).to(DEV)
+    st = new_gpu_state(n, True, fill=0.5)
+    g = synth.stored_grad(n, 1e-3, 1.0, "f32", (0, "skip", "g")).to(DEV)
+    ra.radamw_step_inplace(p, g, st, opts, ra.control())
+    torch.cuda.synchronize()
+    before = snapshot(p, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq)
+    launches = ra.radamw_launch_count()
+    assert not ra.radamw_step_inplace(p, g, st, opts, ra.control(1.0, True))
+    out_p = torch.full_like(p, 7.0)
+    out_s = new_gpu_state(n, True, fill=7.0)
+    out_before = snapshot(out_p, out_s.exp_avg)
+    assert not ra.radamw_step(p, g, st, opts, ra.control(1.0, True), out_p, out_s)
+    torch.cuda.synchronize()
+    assert ra.radamw_launch_count() == launches and st.step == 1 and out_s.step == 0
+    assert unchanged(before, [p, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq])
+    assert unchanged(out_before, [out_p, out_s.exp_avg])
+    e = torch.empty(0, device=DEV)
+    est = ra.AdamWState(3, e, e, e)
+    assert not ra.radamw_step_inplace(e, e, est, opts, ra.control())
+    assert est.step == 3 and ra.radamw_launch_count() == launches
+
+
+def test_resume_from_parts_is_bit_exact():
+    """k steps, copy the step count and moments into fresh buffers, k more ==
+    2k uninterrupted (FA-ja "低レベルの使用": state handed out in parts)."""
+    n, k = 20000, 3
+    opts = ra.options(amsgrad=True, weight_decay=0.01)
+    p0 = synth.normal(n, 0.02, (0, "res", "p"))
+    grads = [synth.stored_grad(n, 1e-3, 128.0, "bf16", (0, "res", "g", t)).to(DEV) for t in range(2 * k)]
+    pa, sa = p0.to(DEV), new_gpu_state(n, True)
+    for g in grads:
+        ra.radamw_step_inplace(pa, g, sa, opts, ra.control(128.0))
+    pb, sb = p0.to(DEV), new_gpu_state(n, True)
+    for g in grads[:k]:
+        ra.radamw_step_inplace(pb, g, sb, opts, ra.control(128.0))
+    torch.cuda.synchronize()
+    pc = pb.clone()
+    sc = ra.AdamWState(sb.step, sb.exp_avg.clone(), sb.exp_avg_sq.clone(), sb.max_exp_avg_sq.clone())
+    del pb, sb
+    for g in grads[k:]:
+        ra.radamw_step_inplace(pc, g, sc, opts, ra.control(128.0))
+    torch.cuda.synchronize()
+    assert sc.step == sa.step == 2 * k
+    assert bits_equal(pc, pa) and bits_equal(sc.exp_avg, sa.exp_avg)
+    assert bits_equal(sc.exp_avg_sq, sa.exp_avg_sq) and bits_equal(sc.max_exp_avg_sq, sa.max_exp_avg_sq)
+
+
+def test_closed_forms_on_gpu():
+    """g = 0 from zero state: p * decay exactly, moments exactly 0; lr = 0:
+    p bit-unchanged; maximize(G) == minimize(-G) bit for bit."""
+    n = 9999
+    p0 = synth.normal(n, 0.02, (0, "cf", "p")).to(DEV)
+    p, st = p0.clone(), new_gpu_state(n, True)
+    zero = torch.zeros(n, device=DEV)
+    opts = ra.options(lr=1e-2, weight_decay=0.1, amsgrad=True)
+    expect = p0.clone()
+    decay = torch.tensor(np.float32(1 - 1e-2 * 0.1), device=DEV)
+    for _ in range(5):
+        ra.radamw_step_inplace(p, zero, st, opts, ra.control())
+        expect = expect * decay
+    torch.cuda.synchronize()
+    assert bits_equal(p, expect)
+    assert not torch.any(st.exp_avg != 0) and not torch.any(st.exp_avg_sq != 0)
+    g = synth.stored_grad(n, 1e-3, 1.0, "f32", (0, "cf", "g")).to(DEV)
+    p1, s1 = p0.clone(), new_gpu_state(n, False)
+    ra.radamw_step_inplace(p1, g, s1, ra.options(lr=0.0, weight_decay=0.5), ra.control())
+    torch.cuda.synchronize()
+    assert bits_equal(p1, p0) and torch.any(s1.exp_avg != 0)
+    pa, sa = p0.clone(), new_gpu_state(n, False)
+    pb, sb = p0.clone(), new_gpu_state(n, False)
+    for _ in range(3):
+        ra.radamw_step_inplace(pa, g, sa, ra.options(maximize=True), ra.control(3.0))
+        ra.radamw_step_inplace(pb, -g, sb, ra.options(maximize=False), ra.control(3.0))
+    torch.cuda.synchronize()
+    assert bits_equal(pa, pb) and bits_equal(sa.exp_avg, sb.exp_avg)
+
+
+# ------------------------------------------------------------ rejections --
+
+def _lib():
+    return ra.load()
+
+
+def test_rejections_leave_everything_untouched():
+    n = 4096
+    lib = _lib()
+    opts = ra.options(amsgrad=True)
+    buf = torch.zeros(5 * n, device=DEV)
+    g = torch.ones(n, device=DEV)
+    p, m, v, x = (buf[i * n:(i + 1) * n] for i in range(4))
+    launches = ra.radamw_launch_count()
+    before = snapshot(buf)
+    upd = ctypes.c_int32(-9)
+
+    def inplace(pp, gg, gdt, st, o=opts):
+        cst = _abi._State(st[0], *st[1:])
+        return lib.radamw_step_inplace(pp, gg, gdt, n, ctypes.byref(cst), ctypes.byref(o),
+                                       ctypes.byref(ra.control()), torch.cuda.current_stream().cuda_stream,
+                                       ctypes.byref(upd)), cst
+
+    # overlapping state (m overlaps v by one element)
+    rc, cst = inplace(p.data_ptr(), g.data_ptr(), 0, (1, m.data_ptr(), m.data_ptr() + 4, x.data_ptr()))
+    assert rc == -3 and cst.step == 1
+    # gradient overlapping a written buffer
+    rc, _ = inplace(p.data_ptr(), m.data_ptr(), 0, (1, m.data_ptr(), v.data_ptr(), x.data_ptr()))
+    assert rc == -3
+    # misaligned gradient pointer
+    rc, _ = inplace(p.data_ptr(), g.data_ptr() + 2, 0, (1, m.data_ptr(), v.data_ptr(), x.data_ptr()))
+    assert rc == -4
+    # host pointer
+    hostbuf = torch.zeros(n)
+    rc, _ = inplace(p.data_ptr(), hostbuf.data_ptr(), 0, (1, m.data_ptr(), v.data_ptr(), x.data_ptr()))
+    assert rc == -1
+    # AMSGrad without v_max
+    rc, _ = inplace(p.data_ptr(), g.data_ptr(), 0, (1, m.data_ptr(), v.data_ptr(), None))
+    assert rc == -2
+    # out of place: output aliasing an input
+    cin = _abi._State(1, m.data_ptr(), v.data_ptr(), x.data_ptr())
+    cout = _abi._State(0, buf[4 * n:].data_ptr(), v.data_ptr(), x.data_ptr())
+    rc = lib.radamw_step(p.data_ptr(), g.data_ptr(), 0, n, ctypes.byref(cin), p.data_ptr(), ctypes.byref(cout),
+                         ctypes.byref(opts), ctypes.byref(ra.control()), torch.cuda.current_stream().cuda_stream,
+                         ctypes.byref(upd))
+    assert rc == -3 and cout.step == 0
+    # multi: two segments sharing a parameter buffer
+    seg = ra.Segment(p, g, m, v, x)
+    with pytest.raises(ra.RadamwError) as e:
+        ra.radamw_step_multi([seg, ra.Segment(p, g, buf[4 * n:], torch.empty(n, device=DEV),
+                                              torch.empty(n, device=DEV))], 1, opts, ra.control())
+    assert e.value.status == -3
+    torch.cuda.synchronize()
+    assert upd.value == -9
+    assert ra.radamw_launch_count() == launches
+    assert unchanged(before, [buf])

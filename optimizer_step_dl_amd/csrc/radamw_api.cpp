@@ -35,8 +35,7 @@ constexpr int MAX_DEVICES = 64;
 
 struct DeviceCache {
     std::mutex mu;
-    int cu_count = 0;
-    // segment-table staging ring (see TableRing below)
+    // segment-table staging ring (see launch_table)
     static constexpr int RING = 8;
     struct Slot {
         void *host = nullptr;
@@ -63,21 +62,6 @@ int stream_device(hipStream_t stream, int *dev) {
     if (d < 0 || d >= MAX_DEVICES) return RADAMW_ERR_INVALID;
     *dev = static_cast<int>(d);
     return RADAMW_OK;
-}
-
-int cu_count(int dev) {
-    DeviceCache &dc = g_devices[dev];
-    std::lock_guard<std::mutex> lock(dc.mu);
-    if (dc.cu_count == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0) {
-            (void)hipGetLastError();
-            cus = 256;  // MI355X
-        }
-        dc.cu_count = cus;
-    }
-    return dc.cu_count;
 }
 
 // ------------------------------------------------------------- validation --
@@ -210,9 +194,8 @@ int32_t segment_head(const SegDesc &s, int gdt, bool amsgrad, bool first) {
     return static_cast<int32_t>(head);
 }
 
-int update_grid(int dev, int64_t tiles) {
-    const int64_t cap = int64_t(cu_count(dev)) * RADAMW_UPDATE_BLOCKS_PER_CU;
-    return static_cast<int>(std::max<int64_t>(1, std::min(tiles, cap)));
+int update_grid(int64_t tiles) {
+    return static_cast<int>(std::max<int64_t>(1, std::min(tiles, UPDATE_MAX_GRID)));
 }
 
 // Validate one tensor's pointers for an update; appends its byte ranges.
@@ -258,7 +241,7 @@ int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, 
                   hipStream_t stream) {
     s.head = segment_head(s, gdt, amsgrad, first);
     s.tile_begin = 0;
-    const int grid = update_grid(dev, segment_tiles(s.n, s.head));
+    const int grid = update_grid(segment_tiles(s.n, s.head));
     int rc = hip_status(launch_update_single(s, c, gdt, amsgrad, first, grid, stream));
     if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
     return rc;
@@ -284,7 +267,7 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     const size_t bytes = desc_bytes + sizeof(int64_t) * (nseg + 1);
 
     DeviceCache &dc = g_devices[dev];
-    const int grid = update_grid(dev, tiles);
+    const int grid = update_grid(tiles);
     std::lock_guard<std::mutex> lock(dc.mu);
     DeviceCache::Slot &slot = dc.slots[dc.next];
     dc.next = (dc.next + 1) % DeviceCache::RING;

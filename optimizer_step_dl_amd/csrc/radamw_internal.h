@@ -8,21 +8,27 @@
 
 namespace radamw {
 
-// Workgroup shape of the update kernels: 256 lanes = 4 wave64s.  Each lane
-// owns UPDATE_UNROLL 16-byte FP32 chunks (4 elements each) per tile.
-constexpr int UPDATE_BLOCK = 256;
+// Workgroup shape of the update kernels: one wave64 per workgroup, each lane
+// owning UPDATE_UNROLL 16-byte FP32 chunks (4 elements) of every stream per
+// tile, and one tile per workgroup.  Measured on MI355X (2^28-element
+// buckets, 4-read/3-write streams): many small single-tile workgroups keep
+// the most independent requests in flight; 64 lanes x 1 chunk reached
+// ~6.3-6.4 TB/s where 256 lanes x 4 chunks with a grid-stride loop reached
+// ~5.6 TB/s.
+#ifndef RADAMW_UPDATE_BLOCK
+#define RADAMW_UPDATE_BLOCK 64
+#endif
+constexpr int UPDATE_BLOCK = RADAMW_UPDATE_BLOCK;
 #ifndef RADAMW_UPDATE_UNROLL
-#define RADAMW_UPDATE_UNROLL 4
+#define RADAMW_UPDATE_UNROLL 1
 #endif
 constexpr int UPDATE_UNROLL = RADAMW_UPDATE_UNROLL;
 constexpr int64_t UPDATE_TILE_CHUNKS = int64_t(UPDATE_BLOCK) * UPDATE_UNROLL;  // float4 chunks per tile
 constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 
-// Grid cap of the update kernels, in workgroups per compute unit; the kernels
-// stride over tiles when there are more tiles than workgroups.
-#ifndef RADAMW_UPDATE_BLOCKS_PER_CU
-#define RADAMW_UPDATE_BLOCKS_PER_CU 8
-#endif
+// Grid of the update kernels: one workgroup per tile, up to this many
+// workgroups; beyond it the kernels stride over tiles.
+constexpr int64_t UPDATE_MAX_GRID = 0x7fffffff;
 
 // Statistics: 256-lane analysis workgroups, each lane loads STATS_UNROLL
 // 16-byte chunks per pass; one record ("row") per workgroup.

@@ -192,7 +192,8 @@ def main(argv=None):
     # ------------------------------------------------ update-only variants --
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
-         "adamw_f32_firststep"] if args.variants == "all" else args.variants.split(","))
+         "adamw_f32_firststep"] if args.variants == "all" else
+        [v for v in args.variants.split(",") if v != "decoder_1b"])
     variants = {}
     for name in wanted:
         variant, gdt, mode = name.split("_")
@@ -238,6 +239,11 @@ def main(argv=None):
         torch.cuda.empty_cache()
 
     # --------------------------------------------------- copy ceiling --
+    # ----------------------------- tensor list: per-tensor vs one launch --
+    decoder = None
+    if args.variants == "all" or "decoder_1b" in args.variants.split(","):
+        decoder = bench_decoder_list(torch, synth, ra, dev, stream)
+
     # A plain elementwise copy of known size (1 GiB read, 1 GiB written):
     # torch's unary negation kernel.  It is the calibration kernel for the
     # rocprofv3 HBM counters and, timed, a context ceiling for streaming.
@@ -293,11 +299,60 @@ def main(argv=None):
         "kernels": kernels,
         "variants": variants,
         "copy_ceiling": copy_ceiling,
+        "decoder_1b_list": decoder,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip},
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def bench_decoder_list(torch, synth, ra, dev, stream):
+    """201 tensors shaped like a 1.1B decoder, FP16 grads (N(0,1e-4) x 1024,
+    scale 1024), AMSGrad at t = 50: 201 per-tensor launches (the pages'
+    torch front-end launches one update kernel per parameter) against one
+    radamw_step_multi launch over the same list."""
+    shapes = synth.decoder_1b_shapes()
+    n_total = synth.total(shapes)
+    segs = []
+    for i, (_, n) in enumerate(shapes):
+        key = (0, "dec1b-bench", i)
+        p = synth.normal(n, 0.02, key + ("p",), dev)
+        g = synth.stored_grad(n, 1e-4, 1024.0, "f16", key + ("g",), dev)
+        m, v, vmax = synth.steady_state(n, key, True, dev, m_std=1e-5, v_root_std=1e-4)
+        segs.append(ra.Segment(p, g, m, v, vmax))
+    opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=True)
+    ctrl = ra.control(1024.0)
+    states = [ra.AdamWState(49, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq) for s in segs]
+
+    def per_tensor():
+        for s, st in zip(segs, states):
+            st.step = 49
+            ra.radamw_step_inplace(s.param, s.grad, st, opts, ctrl)
+
+    def one_launch():
+        ra.radamw_step_multi(segs, 49, opts, ctrl)
+
+    out = {"tensors": len(shapes), "n_params": n_total, "bytes_per_param": 34}
+    for name, fn in (("per_tensor", per_tensor), ("one_launch", one_launch)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / 10
+        ms = e0.elapsed_time(e1) / 10
+        out[name] = {"device_ms": ms, "wall_ms": wall * 1e3, "params_per_s": n_total / (ms * 1e-3),
+                     "gbs": 34 * n_total / (ms * 1e-3) / 1e9}
+        log(f"decoder 1.1B list {name}: {ms:.3f} ms device, {wall * 1e3:.3f} ms wall, {out[name]['gbs']:.0f} GB/s")
+    del segs, states
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(torch, synth, seconds):

@@ -263,8 +263,23 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
         tiles += segment_tiles(segs[i].n, segs[i].head);
     }
     prefix[nseg] = tiles;
+    // coarse[j] = the (non-empty) segment holding tile j << TABLE_COARSE_LOG2;
+    // the last entry closes the range with the last segment.
+    const int64_t ncoarse = ((tiles - 1) >> TABLE_COARSE_LOG2) + 1;
+    std::vector<int32_t> coarse(ncoarse + 1);
+    {
+        int32_t s = 0;
+        for (int64_t j = 0; j < ncoarse; ++j) {
+            const int64_t t = j << TABLE_COARSE_LOG2;
+            while (prefix[s + 1] <= t) ++s;
+            coarse[j] = s;
+        }
+        coarse[ncoarse] = nseg - 1;
+    }
     const size_t desc_bytes = sizeof(SegDesc) * nseg;
-    const size_t bytes = desc_bytes + sizeof(int64_t) * (nseg + 1);
+    const size_t prefix_bytes = sizeof(int64_t) * (nseg + 1);
+    const size_t coarse_bytes = sizeof(int32_t) * (ncoarse + 1);
+    const size_t bytes = desc_bytes + prefix_bytes + coarse_bytes;
 
     DeviceCache &dc = g_devices[dev];
     const int grid = update_grid(tiles);
@@ -296,13 +311,17 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
         }
         slot.cap = cap;
     }
-    std::memcpy(slot.host, segs.data(), desc_bytes);
-    std::memcpy(static_cast<char *>(slot.host) + desc_bytes, prefix.data(), sizeof(int64_t) * (nseg + 1));
+    char *host = static_cast<char *>(slot.host);
+    std::memcpy(host, segs.data(), desc_bytes);
+    std::memcpy(host + desc_bytes, prefix.data(), prefix_bytes);
+    std::memcpy(host + desc_bytes + prefix_bytes, coarse.data(), coarse_bytes);
     hipError_t e = hipMemcpyAsync(slot.dev, slot.host, bytes, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_status(e);
-    const SegDesc *d_segs = static_cast<const SegDesc *>(slot.dev);
-    const int64_t *d_prefix = reinterpret_cast<const int64_t *>(static_cast<const char *>(slot.dev) + desc_bytes);
-    e = launch_update_table(d_segs, d_prefix, nseg, tiles, c, gdt, amsgrad, first, grid, stream);
+    const char *dev_base = static_cast<const char *>(slot.dev);
+    const SegDesc *d_segs = reinterpret_cast<const SegDesc *>(dev_base);
+    const int64_t *d_prefix = reinterpret_cast<const int64_t *>(dev_base + desc_bytes);
+    const int32_t *d_coarse = reinterpret_cast<const int32_t *>(dev_base + desc_bytes + prefix_bytes);
+    e = launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid, stream);
     if (e != hipSuccess) return hip_status(e);
     g_launches.fetch_add(1, std::memory_order_relaxed);
     e = hipEventRecord(slot.done, stream);

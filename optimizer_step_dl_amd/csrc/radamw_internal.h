@@ -26,6 +26,10 @@ constexpr int UPDATE_UNROLL = RADAMW_UPDATE_UNROLL;
 constexpr int64_t UPDATE_TILE_CHUNKS = int64_t(UPDATE_BLOCK) * UPDATE_UNROLL;  // float4 chunks per tile
 constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 
+// Coarse index of the multi-tensor kernel: one entry per 2^10 tiles
+// (256K elements), naming the segment that holds that tile.
+constexpr int TABLE_COARSE_LOG2 = 10;
+
 // Grid of the update kernels: one workgroup per tile, up to this many
 // workgroups; beyond it the kernels stride over tiles.
 constexpr int64_t UPDATE_MAX_GRID = 0x7fffffff;
@@ -87,13 +91,27 @@ struct StatsRec {
     uint32_t w[3];
 };
 
+// Global-address-space views of generic pointers.  Tensor pointers that
+// reach a kernel through memory (the multi-tensor descriptor table) are
+// generic to the compiler, which would then emit FLAT instructions; these
+// casts make every stream access a global_load / global_store.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *gl(const T *p) {
+    return (const __attribute__((address_space(1))) T *)p;
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *gl(T *p) {
+    return (__attribute__((address_space(1))) T *)p;
+}
+
 // Launchers (host functions defined next to the kernels).  They return the
 // hipError_t of the launch.
 hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
                                 bool first, int grid, hipStream_t stream);
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
-                               int32_t nseg, int64_t total_tiles, const Coefs &c, int gdt,
-                               bool amsgrad, bool first, int grid, hipStream_t stream);
+                               const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
+                               const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
+                               hipStream_t stream);
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream);
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,

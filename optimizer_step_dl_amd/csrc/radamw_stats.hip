@@ -39,16 +39,16 @@ __device__ __forceinline__ void acc_value(Acc &a, int slot, float x) {
 template <int GDT>
 __device__ __forceinline__ void acc_chunk(Acc &a, const void *g, int64_t chunk) {
     if constexpr (GDT == G_F32) {
-        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(g) + chunk);
+        const f32x4 x = __builtin_nontemporal_load(gl(reinterpret_cast<const f32x4 *>(g)) + chunk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc_value(a, j, x[j]);
     } else if constexpr (GDT == G_F16) {
-        const f16x8 h = __builtin_nontemporal_load(reinterpret_cast<const f16x8 *>(g) + chunk);
+        const f16x8 h = __builtin_nontemporal_load(gl(reinterpret_cast<const f16x8 *>(g)) + chunk);
         const f32x8 x = __builtin_convertvector(h, f32x8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc_value(a, j & 3, x[j]);
     } else {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(g) + chunk);
+        const u32x4 w = __builtin_nontemporal_load(gl(reinterpret_cast<const u32x4 *>(g)) + chunk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             acc_value(a, j, __builtin_bit_cast(float, w[j] << 16));
@@ -59,9 +59,9 @@ __device__ __forceinline__ void acc_chunk(Acc &a, const void *g, int64_t chunk) 
 
 template <int GDT>
 __device__ __forceinline__ float load_one(const void *g, int64_t e) {
-    if constexpr (GDT == G_F32) return static_cast<const float *>(g)[e];
-    else if constexpr (GDT == G_F16) return static_cast<float>(static_cast<const _Float16 *>(g)[e]);
-    else return __builtin_bit_cast(float, uint32_t(static_cast<const uint16_t *>(g)[e]) << 16);
+    if constexpr (GDT == G_F32) return gl(static_cast<const float *>(g))[e];
+    else if constexpr (GDT == G_F16) return static_cast<float>(gl(static_cast<const _Float16 *>(g))[e]);
+    else return __builtin_bit_cast(float, uint32_t(gl(static_cast<const uint16_t *>(g))[e]) << 16);
 }
 
 __device__ __forceinline__ double wave_sum(double v) {

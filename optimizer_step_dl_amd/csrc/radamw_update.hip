@@ -38,18 +38,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
 #if RADAMW_NT_LOADS
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load(gl(p));
 #else
-    return *p;
+    return *gl(p);
 #endif
 }
 
 template <typename T>
 __device__ __forceinline__ void stream_store(T *p, T v) {
 #if RADAMW_NT_STORES
-    __builtin_nontemporal_store(v, p);
+    __builtin_nontemporal_store(v, gl(p));
 #else
-    *p = v;
+    *gl(p) = v;
 #endif
 }
 
@@ -80,11 +80,11 @@ __device__ __forceinline__ f32x4 load_grad4(const void *g, int64_t e) {
 template <int GDT>
 __device__ __forceinline__ float load_grad1(const void *g, int64_t e) {
     if constexpr (GDT == G_F32) {
-        return static_cast<const float *>(g)[e];
+        return gl(static_cast<const float *>(g))[e];
     } else if constexpr (GDT == G_F16) {
-        return static_cast<float>(static_cast<const _Float16 *>(g)[e]);
+        return static_cast<float>(gl(static_cast<const _Float16 *>(g))[e]);
     } else {
-        return bf16_bits_to_float(uint32_t(static_cast<const uint16_t *>(g)[e]) << 16);
+        return bf16_bits_to_float(uint32_t(gl(static_cast<const uint16_t *>(g))[e]) << 16);
     }
 }
 
@@ -116,18 +116,18 @@ __device__ __forceinline__ void adamw_element(float x, float &p, float &m, float
 template <int GDT, bool AMS, bool FIRST>
 __device__ __forceinline__ void scalar_element(const SegDesc &s, int64_t e, const Coefs &c) {
     float x = load_grad1<GDT>(s.g, e);
-    float p = s.p_in[e];
+    float p = gl(s.p_in)[e];
     float m = 0.0f, v = 0.0f, vmax = 0.0f;
     if constexpr (!FIRST) {
-        m = s.m_in[e];
-        v = s.v_in[e];
-        if constexpr (AMS) vmax = s.vmax_in[e];
+        m = gl(s.m_in)[e];
+        v = gl(s.v_in)[e];
+        if constexpr (AMS) vmax = gl(s.vmax_in)[e];
     }
     adamw_element<AMS, FIRST>(x, p, m, v, vmax, c);
-    s.p_out[e] = p;
-    s.m_out[e] = m;
-    s.v_out[e] = v;
-    if constexpr (AMS) s.vmax_out[e] = vmax;
+    gl(s.p_out)[e] = p;
+    gl(s.m_out)[e] = m;
+    gl(s.v_out)[e] = v;
+    if constexpr (AMS) gl(s.vmax_out)[e] = vmax;
 }
 
 // One tile of a mutually aligned segment: UPDATE_UNROLL 16-byte chunks per
@@ -242,16 +242,20 @@ __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, C
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) any_tile<GDT, AMS, FIRST>(s, t, c);
 }
 
-// A list of tensors in one launch: descriptors and the tile prefix sums live
-// in device memory; each workgroup finds its first segment by binary search
-// and then advances a cursor, since its tiles only move forward.
+// A list of tensors in one launch.  Descriptors, tile prefix sums and a
+// coarse index live in device memory: coarse[j] is the segment holding tile
+// j << TABLE_COARSE_LOG2, so a workgroup's segment lies in
+// [coarse[j], coarse[j + 1]] and is found with one load and a short binary
+// search (usually over one or two segments), instead of a search over the
+// whole list before every 256-element tile.
 template <int GDT, bool AMS, bool FIRST>
 __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_table(
-    const SegDesc *__restrict__ segs, const int64_t *__restrict__ prefix, int32_t nseg,
-    int64_t total_tiles, Coefs c) {
+    const SegDesc *__restrict__ segs, const int64_t *__restrict__ prefix,
+    const int32_t *__restrict__ coarse, int32_t nseg, int64_t total_tiles, Coefs c) {
     int64_t t = blockIdx.x;
     if (t >= total_tiles) return;
-    int32_t lo = 0, hi = nseg;  // prefix[lo] <= t < prefix[hi]
+    const int64_t j = t >> TABLE_COARSE_LOG2;
+    int32_t lo = coarse[j], hi = coarse[j + 1] + 1;  // prefix[lo] <= t < prefix[hi]
     while (hi - lo > 1) {
         const int32_t mid = (lo + hi) >> 1;
         if (prefix[mid] <= t) lo = mid; else hi = mid;
@@ -273,10 +277,10 @@ static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, int grid, 
 }
 
 template <int GDT, bool AMS, bool FIRST>
-static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, int32_t nseg,
-                                 int64_t total, const Coefs &c, int grid, hipStream_t st) {
+static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, const int32_t *coarse,
+                                 int32_t nseg, int64_t total, const Coefs &c, int grid, hipStream_t st) {
     hipLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
-                       st, segs, prefix, nseg, total, c);
+                       st, segs, prefix, coarse, nseg, total, c);
     return hipGetLastError();
 }
 
@@ -303,9 +307,11 @@ hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, boo
 }
 
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
-                               int32_t nseg, int64_t total_tiles, const Coefs &c, int gdt,
-                               bool amsgrad, bool first, int grid, hipStream_t stream) {
-    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, nseg, total_tiles, c, grid, stream)
+                               const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
+                               const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
+                               hipStream_t stream) {
+    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, nseg, total_tiles, c, grid,
+                    stream)
 }
 
 }  // namespace radamw

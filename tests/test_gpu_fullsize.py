@@ -1,0 +1,216 @@
+"""Full-size GPU parity: the 2^28 bucket, the 1.1B-parameter 201-tensor list
+and the 6.7B-parameter 291-tensor list with statistics, clipping and an
+injected non-finite step.
+
+At these sizes the oracle checks sampled elements one by one (inputs gathered
+before the step, outputs gathered after it) and, for the statistics, every
+element (streamed tensor by tensor through the C oracle).  Whole-array
+properties (finiteness, AMSGrad max, bit-identity between launch forms) are
+checked on the device.
+
+Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGrad",
+TR-zh = "训练与状态保存"."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import optimizer_step_dl_amd as ra
+from gpu_helpers import DEV, announce, bits_equal, contract_one_step, grad_host, oracle_opts
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_idx(n, k, key):
+    rng = np.random.Generator(np.random.PCG64(synth.derive_seed(*key)))
+    idx = np.concatenate([np.arange(min(n, 1024)), np.arange(max(0, n - 1024), n), rng.integers(0, n, size=k)])
+    return np.unique(idx)
+
+
+def _gather(t, idx_dev):
+    return None if t is None else t.index_select(0, idx_dev).cpu()
+
+
+def _oracle_on_sample(p, g, m, v, vmax, step, opts, scale, gdt):
+    """Run the oracle on gathered host copies; returns (p, state)."""
+    pp = p.numpy().copy()
+    st = oracle.State(pp.size, vmax is not None)
+    st.step = step
+    if step > 0:
+        st.exp_avg = m.numpy().copy()
+        st.exp_avg_sq = v.numpy().copy()
+        if vmax is not None:
+            st.max_exp_avg_sq = vmax.numpy().copy()
+    oracle.adamw_step(pp, synth.grad_numpy(g), gdt, st, oracle_opts(opts), scale)
+    return pp, st
+
+
+@pytest.mark.parametrize("variant,gdt,mode", [
+    ("adamw", "f32", "inplace"), ("adamw", "f32", "outofplace"), ("amsgrad", "f32", "inplace"),
+    ("amsgrad", "f32", "outofplace"), ("adamw", "bf16", "inplace")])
+def test_bucket_2pow28_steady_state(variant, gdt, mode):
+    """The 268,435,456-element bucket at t = 1000 as bench.py builds it,
+    launched as bench.py launches it (one-segment radamw_step_multi in place,
+    radamw_step out of place); oracle on 67k sampled elements incl. both ends."""
+    n = 1 << 28
+    announce(f"bucket 2^28 {variant} {gdt} {mode}")
+    amsgrad = variant == "amsgrad"
+    key = (0, "bucket", n)
+    p = synth.normal(n, 0.02, key + ("p",), DEV)
+    g = synth.stored_grad(n, 1e-3, 1.0, gdt, key + ("g",), DEV)
+    m, v, vmax = synth.steady_state(n, key, amsgrad, DEV, m_std=1e-4, v_root_std=1e-3)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
+    idx = _sample_idx(n, 65536, (0, "bucket-sample"))
+    idx_dev = torch.from_numpy(idx).to(DEV)
+    before = [_gather(t, idx_dev) for t in (p, g, m, v, vmax)]
+    if mode == "inplace":
+        updated, step = ra.radamw_step_multi([ra.Segment(p, g, m, v, vmax)], 999, opts, ra.control(1.0))
+        assert updated and step == 1000
+        outs = (p, m, v, vmax)
+    else:
+        outs = (torch.empty_like(p), torch.empty_like(m), torch.empty_like(v),
+                torch.empty_like(vmax) if amsgrad else None)
+        st_out = ra.AdamWState(0, outs[1], outs[2], outs[3])
+        assert ra.radamw_step(p, g, ra.AdamWState(999, m, v, vmax), opts, ra.control(1.0), outs[0], st_out)
+        assert st_out.step == 1000
+        # inputs untouched by an out-of-place step
+        assert bits_equal(_gather(p, idx_dev), before[0]) and bits_equal(_gather(m, idx_dev), before[2])
+    torch.cuda.synchronize()
+    p_ref, st_ref = _oracle_on_sample(*before, 999, opts, 1.0, gdt)
+    after = [_gather(t, idx_dev) for t in outs]
+    contract_one_step(after[0].numpy(), p_ref, "p")
+    contract_one_step(after[1].numpy(), st_ref.exp_avg, "m")
+    contract_one_step(after[2].numpy(), st_ref.exp_avg_sq, "v")
+    if amsgrad:
+        contract_one_step(after[3].numpy(), st_ref.max_exp_avg_sq, "vmax")
+        assert bool(torch.all(outs[3] >= outs[2]))
+    assert bool(torch.isfinite(outs[0]).all()) and bool(torch.isfinite(outs[1]).all())
+
+
+def _decoder_segments(shapes, gdt, scale, amsgrad, step, key, std):
+    """Pre-warmed state for t = step + 1: m ~ N(0, 0.1 sigma), v = N(0, sigma)^2,
+    v_max = v * U(1, 1.5), sigma the unscaled gradient's standard deviation."""
+    segs = []
+    for i, (name, n) in enumerate(shapes):
+        p = synth.normal(n, 0.02, key + (i, "p"), DEV)
+        g = synth.stored_grad(n, std, scale, gdt, key + (i, "g"), DEV)
+        if step > 0:
+            m, v, vmax = synth.steady_state(n, key + (i,), amsgrad, DEV, m_std=0.1 * std, v_root_std=std)
+        else:
+            m, v = torch.empty(n, device=DEV), torch.empty(n, device=DEV)
+            vmax = torch.empty(n, device=DEV) if amsgrad else None
+        segs.append(ra.Segment(p, g, m, v, vmax))
+    return segs
+
+
+@pytest.mark.parametrize("odd", [False, True])
+def test_decoder_1b_list_one_launch_vs_per_tensor(odd):
+    """201 tensors shaped like a 1.1B decoder (odd variant: norms 2047/2049),
+    FP16 grads N(0,1e-4)*1024 with scale 1024, AMSGrad, t = 50: one
+    radamw_step_multi launch == 201 radamw_step_inplace launches bit for bit,
+    and both match the oracle on sampled elements of every tensor."""
+    shapes = synth.decoder_1b_shapes(odd)
+    announce(f"decoder 1.1B list odd={odd}")
+    opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=True)
+    scale = 1024.0
+    segs = _decoder_segments(shapes, "f16", scale, True, 49, (0, "dec1b", odd), 1e-4)
+    twins = [ra.Segment(s.param.clone(), s.grad, s.exp_avg.clone(), s.exp_avg_sq.clone(), s.max_exp_avg_sq.clone())
+             for s in segs]
+    samples = []
+    for i, s in enumerate(segs):
+        n = s.param.numel()
+        idx = torch.from_numpy(_sample_idx(n, 2048, (0, "dec1b-sample", i))).to(DEV)
+        samples.append((idx, [_gather(t, idx) for t in (s.param, s.grad, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)]))
+    launches = ra.radamw_launch_count()
+    updated, step = ra.radamw_step_multi(segs, 49, opts, ra.control(scale))
+    assert updated and step == 50 and ra.radamw_launch_count() == launches + 1
+    for tw in twins:
+        assert ra.radamw_step_inplace(tw.param, tw.grad, ra.AdamWState(49, tw.exp_avg, tw.exp_avg_sq, tw.max_exp_avg_sq),
+                                      opts, ra.control(scale))
+    torch.cuda.synchronize()
+    for i, (s, tw) in enumerate(zip(segs, twins)):
+        assert bits_equal(s.param, tw.param) and bits_equal(s.exp_avg, tw.exp_avg), shapes[i][0]
+        assert bits_equal(s.exp_avg_sq, tw.exp_avg_sq) and bits_equal(s.max_exp_avg_sq, tw.max_exp_avg_sq)
+        idx, before = samples[i]
+        p_ref, st_ref = _oracle_on_sample(*before, 49, opts, scale, "f16")
+        contract_one_step(_gather(s.param, idx).numpy(), p_ref, f"{shapes[i][0]} p")
+        contract_one_step(_gather(s.exp_avg, idx).numpy(), st_ref.exp_avg, f"{shapes[i][0]} m")
+        contract_one_step(_gather(s.max_exp_avg_sq, idx).numpy(), st_ref.max_exp_avg_sq, f"{shapes[i][0]} vmax")
+
+
+def _oracle_stats(segs):
+    acc = oracle.StatsAccumulator()
+    for s in segs:
+        acc.add(grad_host(s.grad), "bf16")
+    return acc.result
+
+
+def test_decoder_7b_list_stats_clip_skip_sequence():
+    """291 tensors shaped like a 6.7B decoder, BF16 grads N(0,1e-4), scale 1,
+    in-place AdamW from no state: fused step (stats -> hierarchical merge ->
+    12-byte read-back -> clip at 1.0 -> update) at t = 1; then a step with
+    round(1e-6 * N) = 6,738 injected +inf/NaN values, which must report
+    exactly that count and skip; then a clean step at t = 2.  Statistics are
+    checked against the oracle over every element; the update on sampled
+    elements of every tensor."""
+    shapes = synth.decoder_7b_shapes()
+    total = synth.total(shapes)
+    announce(f"decoder 6.7B list ({total} params)")
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    oo = oracle_opts(opts)
+    segs = _decoder_segments(shapes, "bf16", 1.0, False, 0, (0, "dec7b"), 1e-4)
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(segs), dtype=torch.uint8, device=DEV)
+    offsets = np.cumsum([0] + [n for _, n in shapes])
+    refs, idxs = [], []
+    for i, s in enumerate(segs):
+        idx = torch.from_numpy(_sample_idx(s.param.numel(), 512, (0, "dec7b-sample", i))).to(DEV)
+        idxs.append(idx)
+        refs.append((_gather(s.param, idx).numpy().copy(), oracle.State(idx.numel(), False)))
+
+    def fused(step, call):
+        announce(f"decoder 6.7B fused call {call}")
+        sumsq, count = _oracle_stats(segs)
+        skip, eff = oracle.decide(sumsq, count, 1.0, 1.0)
+        grads = [_gather(s.grad, idx) for s, idx in zip(segs, idxs)]
+        res, new_step = ra.radamw_fused_step_multi(segs, step, opts, 1.0, 1.0, True, ws)
+        torch.cuda.synchronize()
+        assert res.nonfinite == count and bool(res.found_inf) == skip
+        # The oracle sums 6.7e9 squares left to right in FP64; its a-priori
+        # rounding bound is (n - 1) * 2^-53 ~ 7.5e-7 relative, and with bf16
+        # squares its rounding is one-sided (odd squares are 1 mod 8), so it
+        # drifts low by ~5e-9 here.  The GPU's tree sums are exact to ~1e-15
+        # (pinned against fsum-exact sums in the statistics tests).
+        assert abs(res.sumsq - sumsq) <= (total - 1) * 2.0**-53 * sumsq
+        assert bool(res.updated) == (not skip) and new_step == step + (0 if skip else 1)
+        for (p_ref, st_ref), gr in zip(refs, grads):
+            oracle.adamw_step(p_ref, synth.grad_numpy(gr), "bf16", st_ref, oo, eff, skip)
+        for i, (s, idx) in enumerate(zip(segs, idxs)):
+            p_ref, st_ref = refs[i]
+            contract_one_step(_gather(s.param, idx).numpy(), p_ref, f"{shapes[i][0]} p call {call}")
+            contract_one_step(_gather(s.exp_avg_sq, idx).numpy(), st_ref.exp_avg_sq, f"{shapes[i][0]} v call {call}")
+        return res, new_step
+
+    res, step = fused(0, 1)
+    assert step == 1 and 0.0 < res.clip_coef < 1.0  # norm ~ sqrt(N) * 1e-4 ~ 8.2 > 1
+    # injected step: fresh grads with 6,738 non-finite values at seeded global positions
+    k = round(1e-6 * total)
+    pos = synth.nonfinite_positions(total, k, (0, "dec7b", "inject"))
+    vals = synth.nonfinite_values(k)
+    for i, s in enumerate(segs):
+        s.grad.copy_(synth.stored_grad(s.grad.numel(), 1e-4, 1.0, "bf16", (0, "dec7b", i, "g2"), DEV))
+        lo, hi = np.searchsorted(pos, [offsets[i], offsets[i + 1]])
+        if hi > lo:
+            local = torch.from_numpy(pos[lo:hi] - offsets[i]).to(DEV)
+            s.grad[local] = torch.tensor(vals[lo:hi], dtype=torch.bfloat16, device=DEV)
+    launches = ra.radamw_launch_count()
+    snap = [s.param[:4096].clone() for s in segs]
+    res, step = fused(step, 2)
+    assert res.found_inf and res.nonfinite == k == 6738 and step == 1 and not res.updated
+    assert all(bits_equal(a, s.param[:4096]) for a, s in zip(snap, segs))
+    assert ra.radamw_launch_count() > launches  # statistics ran; the update did not
+    # clean step at t = 2
+    for i, s in enumerate(segs):
+        s.grad.copy_(synth.stored_grad(s.grad.numel(), 1e-4, 1.0, "bf16", (0, "dec7b", i, "g3"), DEV))
+    res, step = fused(step, 3)
+    assert step == 2 and res.updated and not res.found_inf

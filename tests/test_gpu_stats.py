@@ -7,6 +7,7 @@ Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGra
 TR-zh = "训练与状态保存"."""
 import math
 
+
 import numpy as np
 import pytest
 import torch
@@ -52,9 +53,19 @@ def _stats_gpu(grads, hierarchical=True):
     return rep.sumsq, rep.nonfinite, rows_total
 
 
+def sequential_bound(n: int) -> float:
+    """A-priori relative error bound of a left-to-right FP64 sum of n
+    non-negative terms (the oracle's order): (n - 1) * 2^-53."""
+    return max(n - 1, 1) * 2.0**-53
+
+
 @pytest.mark.parametrize("gdt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("n", [1, 7, 8, 9, 4096, 8193, 100003, 3_000_001])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 4096, 8193, 100003, 3_000_001, 40_000_003])
 def test_grad_stats_single_tensor(gdt, n):
+    """Counts bit-exact against the oracle; the GPU's sum within 1e-12 of the
+    exactly rounded sum (math.fsum); the oracle's sequential sum within its
+    own rounding bound.  40,000,003 elements put every analysis workgroup on
+    several passes (rows capped at 2048) with a ragged tail."""
     announce(f"stats {gdt} n={n}")
     g = synth.stored_grad(n, 1e-2, 64.0, gdt, (0, "st", gdt, n)).to(DEV)
     k = min(n // 3, 11)
@@ -62,10 +73,13 @@ def test_grad_stats_single_tensor(gdt, n):
         _inject(g, k, (0, "st", gdt, n, "pos"))
     gh = grad_host(g)
     s_ref, c_ref = oracle.grad_stats(gh, gdt)
-    s_gpu, c_gpu, _ = _stats_gpu([g])
+    s_gpu, c_gpu, rows = _stats_gpu([g])
     assert c_gpu == c_ref == k
     exact = _exact_sumsq(gh, gdt)
-    assert abs(s_gpu - exact) <= 1e-12 * exact and abs(s_ref - exact) <= 1e-12 * exact
+    assert abs(s_gpu - exact) <= 1e-12 * exact
+    assert abs(s_ref - exact) <= sequential_bound(n) * exact
+    if n > 2048 * 8192:
+        assert rows == 2048
 
 
 def test_grad_stats_list_hierarchical_vs_flat_and_deterministic():
@@ -83,7 +97,8 @@ def test_grad_stats_list_hierarchical_vs_flat_and_deterministic():
     assert rows > 1024  # at least one intermediate merge level
     assert c_h == c_f == c_ref == 5
     assert s_h == s_h2 and c_h2 == c_h  # bit-identical repeat
-    assert abs(s_h - s_ref) <= 2e-12 * s_ref and abs(s_f - s_ref) <= 2e-12 * s_ref
+    tol = sequential_bound(sum(sizes)) + 1e-12
+    assert abs(s_h - s_ref) <= tol * s_ref and abs(s_f - s_ref) <= tol * s_ref
 
 
 @pytest.mark.parametrize("nrows", [1, 1024, 1025, 1048576, 1048577, 4194304])
@@ -140,7 +155,7 @@ def _fused_case(sizes, gdt, inject, max_norm, key, step0=0, amsgrad=False, hiera
     res, step = ra.radamw_fused_step_multi(segs, step0, opts, scale, max_norm, hierarchical, ws)
     torch.cuda.synchronize()
     assert res.nonfinite == c_ref and bool(res.found_inf) == skip_ref
-    assert abs(res.sumsq - s_ref) <= 2e-12 * max(s_ref, 1e-300)
+    assert abs(res.sumsq - s_ref) <= (sequential_bound(sum(sizes)) + 1e-12) * max(s_ref, 1e-300)
     launched = ra.radamw_launch_count() - before
     nstats = len([n for n in sizes if n])
     if skip_ref:

@@ -139,6 +139,10 @@ def main(argv=None):
     def one_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
+            # the update kernel's own start/end (hipExtLaunchKernelGGL events):
+            # the launch follows the read-back synchronisation, so events
+            # recorded from the host around it would also time the submission
+            lib.radamw_time_next_update(ev[2].cuda_event, ev[3].cuda_event)
         check(lib.radamw_grad_stats(g.data_ptr(), 0, n, rows.data_ptr(), rows_n, ctypes.byref(written), sptr),
               "grad_stats")
         check(lib.radamw_merge_stats(rows.data_ptr(), rows_n, scratch.data_ptr(), se, report.data_ptr(), 1, sptr),
@@ -150,17 +154,16 @@ def main(argv=None):
                                 ctypes.byref(result)), "decide")
         if ctrl.skip_update:
             raise RuntimeError("unexpected non-finite gradient in the benchmark bucket")
-        if ev is not None:
-            ev[2].record(stream)
         check(lib.radamw_step_multi(seg, 1, 0, ctypes.byref(step), ctypes.byref(opts), ctypes.byref(ctrl), sptr,
                                     ctypes.byref(updated)), "step_multi")
-        if ev is not None:
-            ev[3].record(stream)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in events:  # create the device events before handing them to the library
+        for e in ev:
+            e.record(stream)
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -221,10 +224,13 @@ def main(argv=None):
             launch(k)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-        for k, (a, b) in enumerate(ev):
+        for a, b in ev:
             a.record(stream)
-            launch(k)
             b.record(stream)
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(ev):
+            ra.radamw_time_next_update(a, b)
+            launch(k)
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in ev]
         avg = sum(ms) / len(ms)

@@ -52,7 +52,9 @@ typedef struct ihipStream_t *radamw_stream_t;
 enum {
     RADAMW_OK = 0,
     RADAMW_ERR_INVALID = -1, /* null pointer, n < 0, unknown dtype, host pointer,
-                                hyper-parameter out of range, non-finite or
+                                pointer of another device, an array running
+                                past the end of its allocation, hyper-
+                                parameter out of range, non-finite or
                                 non-positive gradient_scale, flag not 0/1     */
     RADAMW_ERR_STATE = -2,   /* AMSGrad flag and v_max presence disagree, or
                                 the step count would overflow                 */
@@ -186,9 +188,14 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
 
 /*
  * In-place update of a list of tensors that share one options struct and
- * one step count, in ONE kernel launch (FA-ja "サポートされている契約": a
- * pre-flattened bucket works only when every element shares the options and
- * the step count).  A flattened bucket is nseg == 1.
+ * one step count (FA-ja "サポートされている契約": a pre-flattened bucket
+ * works only when every element shares the options and the step count).  A
+ * flattened bucket is nseg == 1.  Launches: every tensor of at least 2^22
+ * elements gets a launch of its own and all smaller tensors share a single
+ * launch, so a list of many small tensors costs one launch, while large
+ * tensors keep the single-tensor kernel (which MI355X pipelines back to
+ * back without gaps, and which measured faster than sharing a launch).  All
+ * launches use the same constants and the step count advances once.
  *   segs  : host array of nseg descriptors (device pointers inside).
  *   step  : host, the shared completed-step count; incremented on launch.
  * Segments with n == 0 are ignored; when every segment is empty nothing is
@@ -311,6 +318,17 @@ int radamw_last_hip_error(void);
 /* Total kernel launches made by the library in this process (test hook:
  * proves skip / empty calls launch nothing). */
 uint64_t radamw_launch_count(void);
+
+/*
+ * Measurement hook (not part of the method): the next radamw_step,
+ * radamw_step_inplace, radamw_step_multi or radamw_fused_step_multi call on
+ * this thread that launches an update records start_event when its first
+ * update kernel starts and stop_event when its last update kernel ends
+ * (hipExtLaunchKernelGGL), so the host's submission latency is not timed.
+ * The events are caller-created hipEvent_t of the stream's device; passing
+ * NULL, NULL clears the request.  Always returns RADAMW_OK.
+ */
+int radamw_time_next_update(void *start_event, void *stop_event);
 
 #ifdef __cplusplus
 }

@@ -147,6 +147,7 @@ def load(path: str = LIB_PATH):
         "radamw_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "radamw_last_hip_error": ([], ctypes.c_int),
         "radamw_launch_count": ([], u64),
+        "radamw_time_next_update": ([vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -160,7 +161,7 @@ EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "rada
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
-           "radamw_last_hip_error", "radamw_launch_count")
+           "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update")
 
 
 # ----------------------------------------------------------------- helpers --
@@ -200,26 +201,67 @@ def _grad_code(g: torch.Tensor) -> int:
     return _DTYPE_CODE[g.dtype]
 
 
+def _check_fast(t: torch.Tensor, what: str, dev_index: int, numel: int, dtype=None):
+    """Cheap form of _dense for long tensor lists (same checks)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if t.get_device() != dev_index:
+        raise ValueError(f"{what} is on device {t.get_device()}, expected {dev_index}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what} has {t.numel()} elements, expected {numel}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype} (got {t.dtype})")
+
+
 def _segments(segs: Sequence[Segment], amsgrad: bool):
     arr = (_Segment * max(1, len(segs)))()
     code = None
-    device = None
+    dev_index = None
+    f32 = torch.float32
     for i, s in enumerate(segs):
-        device = device or s.param.device
-        n = s.param.numel()
-        _dense(s.param, f"segment {i} param", torch.float32, device=device)
-        _dense(s.grad, f"segment {i} grad", numel=n, device=device)
+        p = s.param
+        if dev_index is None:
+            if not isinstance(p, torch.Tensor) or not p.is_cuda:
+                raise ValueError(f"segment {i} param must be a device tensor")
+            dev_index = p.get_device()
+        n = p.numel()
+        _check_fast(p, f"segment {i} param", dev_index, n, f32)
+        _check_fast(s.grad, f"segment {i} grad", dev_index, n)
         c = _grad_code(s.grad)
         if code is not None and c != code:
             raise ValueError("all gradients of one call must share a dtype")
         code = c
-        _dense(s.exp_avg, f"segment {i} exp_avg", torch.float32, n, device)
-        _dense(s.exp_avg_sq, f"segment {i} exp_avg_sq", torch.float32, n, device)
+        _check_fast(s.exp_avg, f"segment {i} exp_avg", dev_index, n, f32)
+        _check_fast(s.exp_avg_sq, f"segment {i} exp_avg_sq", dev_index, n, f32)
         if s.max_exp_avg_sq is not None:
-            _dense(s.max_exp_avg_sq, f"segment {i} max_exp_avg_sq", torch.float32, n, device)
-        arr[i] = _Segment(s.param.data_ptr(), s.grad.data_ptr(), s.exp_avg.data_ptr(),
+            _check_fast(s.max_exp_avg_sq, f"segment {i} max_exp_avg_sq", dev_index, n, f32)
+        arr[i] = _Segment(p.data_ptr(), s.grad.data_ptr(), s.exp_avg.data_ptr(),
                           s.exp_avg_sq.data_ptr(), _ptr_or_none(s.max_exp_avg_sq), n)
-    return arr, (F32 if code is None else code), (device or torch.device("cuda", torch.cuda.current_device()))
+    device = torch.device("cuda", torch.cuda.current_device() if dev_index is None else dev_index)
+    return arr, (F32 if code is None else code), device
+
+
+class SegmentList:
+    """A tensor list marshalled once, for repeated multi-tensor steps over
+    the same tensors (optimizer state and parameters normally keep their
+    storage for a whole run).  Holds references to the tensors; the C entry
+    points still validate every pointer on each call."""
+
+    def __init__(self, segments: Sequence[Segment]):
+        self.segments = list(segments)
+        self.array, self.code, self.device = _segments(self.segments, False)
+
+    def __len__(self):
+        return len(self.segments)
+
+
+def _marshal(segments):
+    if isinstance(segments, SegmentList):
+        return segments.array, segments.code, segments.device, len(segments)
+    arr, code, dev = _segments(segments, False)
+    return arr, code, dev, len(segments)
 
 
 # ------------------------------------------------------------- entry points --
@@ -280,15 +322,15 @@ def radamw_step_inplace(param: torch.Tensor, grad: torch.Tensor, state: AdamWSta
     return bool(updated.value)
 
 
-def radamw_step_multi(segments: Sequence[Segment], step: int, opts: Options, ctrl: Control):
-    """One launch over a tensor list sharing options and step count.
-    Returns (updated, new_step)."""
+def radamw_step_multi(segments, step: int, opts: Options, ctrl: Control):
+    """In-place update of a tensor list (a sequence of Segment or a
+    SegmentList) sharing options and step count.  Returns (updated, new_step)."""
     lib = load()
-    arr, code, dev = _segments(segments, bool(opts.amsgrad))
+    arr, code, dev, count = _marshal(segments)
     st = ctypes.c_uint64(step)
     updated = ctypes.c_int32(0)
     with torch.cuda.device(dev):
-        rc = lib.radamw_step_multi(arr, len(segments), code, ctypes.byref(st), ctypes.byref(opts),
+        rc = lib.radamw_step_multi(arr, count, code, ctypes.byref(st), ctypes.byref(opts),
                                    ctypes.byref(ctrl), _stream(dev), ctypes.byref(updated))
     _check(rc, "radamw_step_multi")
     return bool(updated.value), int(st.value)
@@ -360,28 +402,28 @@ def radamw_decide(host_report: Stats, gradient_scale: float, max_grad_norm: Opti
     return ctrl, res
 
 
-def radamw_fused_workspace_bytes(segments: Sequence[Segment]) -> int:
-    arr, code, _ = _segments(segments, False)
-    r = load().radamw_fused_workspace_bytes(arr, len(segments), code)
+def radamw_fused_workspace_bytes(segments) -> int:
+    arr, code, _, count = _marshal(segments)
+    r = load().radamw_fused_workspace_bytes(arr, count, code)
     if r < 0:
         raise RadamwError(int(r), "radamw_fused_workspace_bytes")
     return int(r)
 
 
-def radamw_fused_step_multi(segments: Sequence[Segment], step: int, opts: Options,
+def radamw_fused_step_multi(segments, step: int, opts: Options,
                             gradient_scale: float, max_grad_norm: Optional[float],
                             hierarchical: bool, workspace: Optional[torch.Tensor]):
     """Statistics -> merge -> read-back -> decision -> one update launch.
     Returns (FusedResult, new_step)."""
     lib = load()
-    arr, code, dev = _segments(segments, bool(opts.amsgrad))
+    arr, code, dev, count = _marshal(segments)
     if workspace is not None:
         _dense(workspace, "workspace", device=dev)
     st = ctypes.c_uint64(step)
     res = FusedResult()
     with torch.cuda.device(dev):
         rc = lib.radamw_fused_step_multi(
-            arr, len(segments), code, ctypes.byref(st), ctypes.byref(opts), float(gradient_scale),
+            arr, count, code, ctypes.byref(st), ctypes.byref(opts), float(gradient_scale),
             0.0 if max_grad_norm is None else float(max_grad_norm), int(bool(hierarchical)),
             _ptr_or_none(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
             _stream(dev), ctypes.byref(res))
@@ -409,3 +451,11 @@ def radamw_last_hip_error() -> int:
 
 def radamw_launch_count() -> int:
     return int(load().radamw_launch_count())
+
+
+def radamw_time_next_update(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
+    """Record torch events at the first update kernel's start and the last
+    one's end in the next launching update call on this thread.  The events
+    must already exist on the device (recorded once)."""
+    load().radamw_time_next_update(None if start is None else start.cuda_event,
+                                   None if stop is None else stop.cuda_event)

@@ -13,6 +13,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -22,6 +23,14 @@ namespace {
 
 std::atomic<uint64_t> g_launches{0};
 thread_local int g_last_hip = 0;
+
+// Measurement hook (radamw_time_next_update): events for the next call on
+// this thread that launches an update.
+struct UpdateTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+thread_local UpdateTiming g_timing;
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return RADAMW_OK;
@@ -94,21 +103,53 @@ bool valid_dtype(int gdt) { return gdt == RADAMW_F32 || gdt == RADAMW_F16 || gdt
 
 size_t grad_bytes(int gdt) { return gdt == RADAMW_F32 ? 4 : 2; }
 
-// A device (or managed) allocation of `dev`, aligned to `align` bytes.
-int check_device_ptr(const void *p, size_t align, int dev) {
-    if (!p) return RADAMW_ERR_INVALID;
-    if (reinterpret_cast<uintptr_t>(p) % align != 0) return RADAMW_ERR_ALIGN;
-    hipPointerAttribute_t a;
-    std::memset(&a, 0, sizeof a);
-    hipError_t e = hipPointerGetAttributes(&a, p);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();  // do not leave a sticky error for the caller
-        return RADAMW_ERR_INVALID;
+// Pointer validation for one call.  A pointer must be device (or managed)
+// memory of the stream's device, aligned to its element size, and the bytes
+// the call touches must lie inside the allocation that holds it.  Each
+// allocation is queried once per call (hipPointerGetAttributes and
+// hipMemGetAddressRange); later pointers into an allocation already seen are
+// checked against its cached extent, so a list of many tensors carved from
+// a few allocations costs a few HIP queries, not one per pointer.
+class PtrChecker {
+  public:
+    explicit PtrChecker(int dev) : dev_(dev) {}
+
+    int check(const void *p, size_t align, int64_t bytes) {
+        if (!p) return RADAMW_ERR_INVALID;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        if (a % align != 0) return RADAMW_ERR_ALIGN;
+        const uintptr_t end = a + static_cast<uintptr_t>(bytes > 0 ? bytes : 0);
+        auto it = known_.upper_bound(a);
+        if (it != known_.begin()) {
+            --it;
+            if (a >= it->first && a < it->second) return end <= it->second ? RADAMW_OK : RADAMW_ERR_INVALID;
+        }
+        hipPointerAttribute_t attr;
+        std::memset(&attr, 0, sizeof attr);
+        hipError_t e = hipPointerGetAttributes(&attr, p);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();  // leave no sticky error behind for the caller
+            return RADAMW_ERR_INVALID;
+        }
+        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return RADAMW_ERR_INVALID;
+        if (attr.device != dev_) return RADAMW_ERR_INVALID;
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        e = hipMemGetAddressRange(&base, &size, const_cast<void *>(p));
+        if (e != hipSuccess || !base || size == 0) {
+            (void)hipGetLastError();
+            return RADAMW_OK;  // extent unknown (e.g. managed memory): type and device checked
+        }
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(base), hi = lo + size;
+        if (a < lo || a >= hi) return RADAMW_OK;
+        known_[lo] = hi;
+        return end <= hi ? RADAMW_OK : RADAMW_ERR_INVALID;
     }
-    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return RADAMW_ERR_INVALID;
-    if (a.device != dev) return RADAMW_ERR_INVALID;
-    return RADAMW_OK;
-}
+
+  private:
+    int dev_;
+    std::map<uintptr_t, uintptr_t> known_;  // allocation base -> end
+};
 
 // Byte ranges touched by one call.  Written ranges may overlap nothing;
 // read-only ranges may overlap each other.
@@ -194,27 +235,26 @@ int32_t segment_head(const SegDesc &s, int gdt, bool amsgrad, bool first) {
     return static_cast<int32_t>(head);
 }
 
-int update_grid(int64_t tiles) {
-    return static_cast<int>(std::max<int64_t>(1, std::min(tiles, UPDATE_MAX_GRID)));
-}
+// One workgroup per tile; callers have checked tiles <= UPDATE_MAX_GRID.
+int update_grid(int64_t tiles) { return static_cast<int>(tiles); }
 
 // Validate one tensor's pointers for an update; appends its byte ranges.
 // For an out-of-place call the inputs are read-only ranges and the outputs
 // written ones; in place, the state and parameter ranges are written.
-int check_update_tensor(const SegDesc &s, int gdt, bool amsgrad, bool first, bool inplace, int dev,
-                        std::vector<Range> &ranges) {
+int check_update_tensor(const SegDesc &s, int gdt, bool amsgrad, bool first, bool inplace,
+                        PtrChecker &pc, std::vector<Range> &ranges) {
     const int64_t fb = s.n * 4, gb = s.n * static_cast<int64_t>(grad_bytes(gdt));
     int rc;
-    if (!inplace && (rc = check_device_ptr(s.p_in, 4, dev))) return rc;
-    if ((rc = check_device_ptr(s.g, grad_bytes(gdt), dev))) return rc;
-    if ((rc = check_device_ptr(s.p_out, 4, dev))) return rc;
-    if ((rc = check_device_ptr(s.m_out, 4, dev))) return rc;
-    if ((rc = check_device_ptr(s.v_out, 4, dev))) return rc;
-    if (amsgrad && (rc = check_device_ptr(s.vmax_out, 4, dev))) return rc;
+    if (!inplace && (rc = pc.check(s.p_in, 4, fb))) return rc;
+    if ((rc = pc.check(s.g, grad_bytes(gdt), gb))) return rc;
+    if ((rc = pc.check(s.p_out, 4, fb))) return rc;
+    if ((rc = pc.check(s.m_out, 4, fb))) return rc;
+    if ((rc = pc.check(s.v_out, 4, fb))) return rc;
+    if (amsgrad && (rc = pc.check(s.vmax_out, 4, fb))) return rc;
     if (!first && !inplace) {
-        if ((rc = check_device_ptr(s.m_in, 4, dev))) return rc;
-        if ((rc = check_device_ptr(s.v_in, 4, dev))) return rc;
-        if (amsgrad && (rc = check_device_ptr(s.vmax_in, 4, dev))) return rc;
+        if ((rc = pc.check(s.m_in, 4, fb))) return rc;
+        if ((rc = pc.check(s.v_in, 4, fb))) return rc;
+        if (amsgrad && (rc = pc.check(s.vmax_in, 4, fb))) return rc;
     }
     add_range(ranges, s.g, gb, false);
     if (inplace) {
@@ -238,11 +278,14 @@ int check_update_tensor(const SegDesc &s, int gdt, bool amsgrad, bool first, boo
 }
 
 int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, int dev,
-                  hipStream_t stream) {
+                  hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    (void)dev;
     s.head = segment_head(s, gdt, amsgrad, first);
     s.tile_begin = 0;
-    const int grid = update_grid(segment_tiles(s.n, s.head));
-    int rc = hip_status(launch_update_single(s, c, gdt, amsgrad, first, grid, stream));
+    const int64_t tiles = segment_tiles(s.n, s.head);
+    if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
+    const int grid = update_grid(tiles);
+    int rc = hip_status(launch_update_single(s, c, gdt, amsgrad, first, grid, stream, ev_start, ev_stop));
     if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
     return rc;
 }
@@ -252,7 +295,7 @@ int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, 
 // stream, and the slot is recycled once an event shows the kernel that read
 // it has finished.
 int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
-                 int dev, hipStream_t stream) {
+                 int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int32_t nseg = static_cast<int32_t>(segs.size());
     std::vector<int64_t> prefix(nseg + 1);
     int64_t tiles = 0;
@@ -281,6 +324,7 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     const size_t coarse_bytes = sizeof(int32_t) * (ncoarse + 1);
     const size_t bytes = desc_bytes + prefix_bytes + coarse_bytes;
 
+    if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
     DeviceCache &dc = g_devices[dev];
     const int grid = update_grid(tiles);
     std::lock_guard<std::mutex> lock(dc.mu);
@@ -321,7 +365,8 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     const SegDesc *d_segs = reinterpret_cast<const SegDesc *>(dev_base);
     const int64_t *d_prefix = reinterpret_cast<const int64_t *>(dev_base + desc_bytes);
     const int32_t *d_coarse = reinterpret_cast<const int32_t *>(dev_base + desc_bytes + prefix_bytes);
-    e = launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid, stream);
+    e = launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid, stream,
+                            ev_start, ev_stop);
     if (e != hipSuccess) return hip_status(e);
     g_launches.fetch_add(1, std::memory_order_relaxed);
     e = hipEventRecord(slot.done, stream);
@@ -358,9 +403,25 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
         return RADAMW_OK;
     }
     const Coefs c = make_coefs(o, *step + 1, gradient_scale);
-    int rc = active.size() == 1
-                 ? launch_single(active[0], gdt, o.amsgrad != 0, first, c, dev, stream)
-                 : launch_table(active, gdt, o.amsgrad != 0, first, c, dev, stream);
+    const bool ams = o.amsgrad != 0;
+    // Launch policy: a tensor of at least MULTI_SOLO_MIN elements gets a
+    // launch of its own; all smaller tensors share one launch.
+    std::vector<SegDesc> solo, shared;
+    for (const SegDesc &d : active) (d.n >= MULTI_SOLO_MIN ? solo : shared).push_back(d);
+    const size_t launches = solo.size() + (shared.empty() ? 0 : 1);
+    // measurement events, if requested: start on the first launch, stop on the last
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    size_t k = 0;
+    auto ev_start = [&]() { return k == 0 ? timing.start : nullptr; };
+    auto ev_stop = [&]() { return k + 1 == launches ? timing.stop : nullptr; };
+    int rc = RADAMW_OK;
+    for (const SegDesc &d : solo) {
+        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream, ev_start(), ev_stop()))) return rc;
+        ++k;
+    }
+    if (shared.size() == 1) rc = launch_single(shared[0], gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+    else if (shared.size() > 1) rc = launch_table(shared, gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
     if (rc != RADAMW_OK) return rc;
     *step += 1;
     *updated = 1;
@@ -371,7 +432,9 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
 int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgrad, bool first,
                    int dev, int64_t *active_out) {
     if (nseg < 0 || (nseg > 0 && !segs)) return RADAMW_ERR_INVALID;
+    PtrChecker pc(dev);
     std::vector<Range> ranges;
+    ranges.reserve(static_cast<size_t>(nseg) * 5);
     int64_t active = 0;
     for (int32_t i = 0; i < nseg; ++i) {
         const radamw_segment &s = segs[i];
@@ -386,7 +449,7 @@ int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgr
         d.v_in = d.v_out = s.exp_avg_sq;
         d.vmax_in = d.vmax_out = s.max_exp_avg_sq;
         d.n = s.n;
-        int rc = check_update_tensor(d, gdt, amsgrad, first, true, dev, ranges);
+        int rc = check_update_tensor(d, gdt, amsgrad, first, true, pc, ranges);
         if (rc) return rc;
     }
     if (active_out) *active_out = active;
@@ -525,14 +588,17 @@ int radamw_step(const float *p, const void *g, radamw_dtype gdt, int64_t n, cons
         d.vmax_out = out->max_exp_avg_sq;
         d.n = n;
         std::vector<Range> ranges;
-        if ((rc = check_update_tensor(d, gdt, ams, first, false, dev, ranges))) return rc;
+        PtrChecker pc(dev);
+        if ((rc = check_update_tensor(d, gdt, ams, first, false, pc, ranges))) return rc;
         if ((rc = check_alias(ranges))) return rc;
         if (ctrl->skip_update) {
             *updated = 0;
             return RADAMW_OK;
         }
         const Coefs c = make_coefs(*opts, in->step + 1, ctrl->gradient_scale);
-        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream))) return rc;
+        const UpdateTiming timing = g_timing;
+        g_timing = UpdateTiming{};
+        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream, timing.start, timing.stop))) return rc;
         out->step = in->step + 1;
         *updated = 1;
         return RADAMW_OK;
@@ -615,8 +681,9 @@ int radamw_grad_stats(const void *g, radamw_dtype gdt, int64_t n, radamw_stats *
     if (rows_capacity < rows) return RADAMW_ERR_RANGE;
     int dev, rc;
     if ((rc = stream_device(stream, &dev))) return rc;
-    if ((rc = check_device_ptr(g, grad_bytes(gdt), dev))) return rc;
-    if ((rc = check_device_ptr(rows_out, 4, dev))) return rc;
+    PtrChecker pc(dev);
+    if ((rc = pc.check(g, grad_bytes(gdt), n * static_cast<int64_t>(grad_bytes(gdt))))) return rc;
+    if ((rc = pc.check(rows_out, 4, rows * 12))) return rc;
     std::vector<Range> ranges;
     add_range(ranges, g, n * static_cast<int64_t>(grad_bytes(gdt)), false);
     add_range(ranges, rows_out, rows * 12, true);
@@ -642,9 +709,10 @@ int radamw_merge_stats(const radamw_stats *rows, int64_t nrows, float *scratch,
     if (scratch_elements < need || scratch_elements < 0) return RADAMW_ERR_RANGE;
     int dev;
     if ((rc = stream_device(stream, &dev))) return rc;
-    if ((rc = check_device_ptr(rows, 4, dev))) return rc;
-    if ((rc = check_device_ptr(report, 4, dev))) return rc;
-    if (need > 0 && (rc = check_device_ptr(scratch, 4, dev))) return rc;
+    PtrChecker pc(dev);
+    if ((rc = pc.check(rows, 4, nrows * 12))) return rc;
+    if ((rc = pc.check(report, 4, 12))) return rc;
+    if (need > 0 && (rc = pc.check(scratch, 4, need * 4))) return rc;
     std::vector<Range> ranges;
     add_range(ranges, rows, nrows * 12, false);
     add_range(ranges, report, 12, true);
@@ -660,7 +728,8 @@ int radamw_read_report(const radamw_stats *report, radamw_stats *host_report, ra
     if (!host_report) return RADAMW_ERR_INVALID;
     int dev, rc;
     if ((rc = stream_device(stream, &dev))) return rc;
-    if ((rc = check_device_ptr(report, 4, dev))) return rc;
+    PtrChecker pc(dev);
+    if ((rc = pc.check(report, 4, 12))) return rc;
     return read_report(reinterpret_cast<const StatsRec *>(report), host_report, dev, stream);
 }
 
@@ -726,7 +795,10 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     result->clip_coef = 1.0;
     if (active == 0) return RADAMW_OK;
     if (workspace_bytes < need) return RADAMW_ERR_RANGE;
-    if ((rc = check_device_ptr(workspace, 4, dev))) return rc;
+    {
+        PtrChecker pc(dev);
+        if ((rc = pc.check(workspace, 4, need))) return rc;
+    }
     {
         // the workspace is written; it may overlap no tensor of the step
         std::vector<Range> ranges;
@@ -790,6 +862,12 @@ const char *radamw_status_string(int status) {
 }
 
 int radamw_last_hip_error(void) { return g_last_hip; }
+
+int radamw_time_next_update(void *start_event, void *stop_event) {
+    g_timing.start = static_cast<hipEvent_t>(start_event);
+    g_timing.stop = static_cast<hipEvent_t>(stop_event);
+    return RADAMW_OK;
+}
 
 uint64_t radamw_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
 

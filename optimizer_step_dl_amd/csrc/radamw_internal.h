@@ -26,12 +26,20 @@ constexpr int UPDATE_UNROLL = RADAMW_UPDATE_UNROLL;
 constexpr int64_t UPDATE_TILE_CHUNKS = int64_t(UPDATE_BLOCK) * UPDATE_UNROLL;  // float4 chunks per tile
 constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 
+// Multi-tensor launch policy.  On MI355X, back-to-back launches of large
+// tensors pipeline with no visible gap, and a shared launch across large
+// tensors held in separate allocations measured 7-10% slower than one
+// launch per tensor; for small tensors one shared launch avoids a launch
+// (and its gap) per tensor.  Tensors of at least this many elements are
+// launched on their own, all smaller ones share one launch.
+constexpr int64_t MULTI_SOLO_MIN = int64_t(1) << 22;
+
 // Coarse index of the multi-tensor kernel: one entry per 2^10 tiles
 // (256K elements), naming the segment that holds that tile.
 constexpr int TABLE_COARSE_LOG2 = 10;
 
-// Grid of the update kernels: one workgroup per tile, up to this many
-// workgroups; beyond it the kernels stride over tiles.
+// Grid of the update kernels: exactly one workgroup per tile.  A launch may
+// hold at most this many tiles (~5.5e11 elements, far beyond device memory).
 constexpr int64_t UPDATE_MAX_GRID = 0x7fffffff;
 
 // Statistics: 256-lane analysis workgroups, each lane loads STATS_UNROLL
@@ -106,12 +114,15 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gl(T *p) {
 
 // Launchers (host functions defined next to the kernels).  They return the
 // hipError_t of the launch.
+// start / stop (may be null) are recorded at the kernel's start and end
+// (hipExtLaunchKernelGGL), for measurement.
 hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
-                                bool first, int grid, hipStream_t stream);
+                                bool first, int grid, hipStream_t stream, hipEvent_t start,
+                                hipEvent_t stop);
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
                                const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
-                               hipStream_t stream);
+                               hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream);
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,

@@ -22,6 +22,8 @@
 // streams.  No MFMA: there is no contraction here.
 #include "radamw_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace radamw {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -235,11 +237,11 @@ __device__ __forceinline__ void any_tile(const SegDesc &s, int64_t tile, const C
         scalar_tile<GDT, AMS, FIRST>(s, tile, c);
 }
 
-// One tensor: the descriptor travels in the kernel arguments.
+// One tensor: the descriptor travels in the kernel arguments; workgroup t
+// handles tile t (the host launches exactly one workgroup per tile).
 template <int GDT, bool AMS, bool FIRST>
-__global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, Coefs c,
-                                                                    int64_t ntiles) {
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) any_tile<GDT, AMS, FIRST>(s, t, c);
+__global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, Coefs c) {
+    any_tile<GDT, AMS, FIRST>(s, blockIdx.x, c);
 }
 
 // A list of tensors in one launch.  Descriptors, tile prefix sums and a
@@ -251,36 +253,34 @@ __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, C
 template <int GDT, bool AMS, bool FIRST>
 __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_table(
     const SegDesc *__restrict__ segs, const int64_t *__restrict__ prefix,
-    const int32_t *__restrict__ coarse, int32_t nseg, int64_t total_tiles, Coefs c) {
-    int64_t t = blockIdx.x;
-    if (t >= total_tiles) return;
+    const int32_t *__restrict__ coarse, Coefs c) {
+    const int64_t t = blockIdx.x;  // one workgroup per tile, grid == total_tiles
     const int64_t j = t >> TABLE_COARSE_LOG2;
     int32_t lo = coarse[j], hi = coarse[j + 1] + 1;  // prefix[lo] <= t < prefix[hi]
     while (hi - lo > 1) {
         const int32_t mid = (lo + hi) >> 1;
         if (prefix[mid] <= t) lo = mid; else hi = mid;
     }
-    int32_t s = lo;
-    for (; t < total_tiles; t += gridDim.x) {
-        while (prefix[s + 1] <= t) ++s;
-        const SegDesc seg = segs[s];
-        any_tile<GDT, AMS, FIRST>(seg, t - prefix[s], c);
-    }
+    const SegDesc seg = segs[lo];
+    any_tile<GDT, AMS, FIRST>(seg, t - prefix[lo], c);
 }
 
 template <int GDT, bool AMS, bool FIRST>
-static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, int grid, hipStream_t st) {
-    const int64_t ntiles = segment_tiles(seg.n, seg.head);
-    hipLaunchKernelGGL((adamw_update_single<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
-                       st, seg, c, ntiles);
+static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, int grid, hipStream_t st,
+                                  hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL((adamw_update_single<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
+                          st, start, stop, 0, seg, c);
     return hipGetLastError();
 }
 
 template <int GDT, bool AMS, bool FIRST>
 static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, const int32_t *coarse,
-                                 int32_t nseg, int64_t total, const Coefs &c, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
-                       st, segs, prefix, coarse, nseg, total, c);
+                                 int32_t nseg, int64_t total, const Coefs &c, int grid, hipStream_t st,
+                                 hipEvent_t start, hipEvent_t stop) {
+    (void)nseg;
+    (void)total;
+    hipExtLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
+                          st, start, stop, 0, segs, prefix, coarse, c);
     return hipGetLastError();
 }
 
@@ -302,16 +302,17 @@ static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, con
     }
 
 hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
-                                bool first, int grid, hipStream_t stream) {
-    RADAMW_DISPATCH(launch_single_t, seg, c, grid, stream)
+                                bool first, int grid, hipStream_t stream, hipEvent_t start,
+                                hipEvent_t stop) {
+    RADAMW_DISPATCH(launch_single_t, seg, c, grid, stream, start, stop)
 }
 
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
                                const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, nseg, total_tiles, c, grid,
-                    stream)
+                    stream, start, stop)
 }
 
 }  // namespace radamw

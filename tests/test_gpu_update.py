@@ -366,6 +366,30 @@ def test_rejections_leave_everything_untouched():
     # AMSGrad without v_max
     rc, _ = inplace(p.data_ptr(), g.data_ptr(), 0, (1, m.data_ptr(), v.data_ptr(), None))
     assert rc == -2
+    # an array running past the end of its allocation: a raw 4 MiB hipMalloc
+    # buffer, gradient range starting 3 MiB in and 2 MiB long.  skip_update = 1,
+    # so even a missed check could not launch anything.
+    hip = ctypes.CDLL("libamdhip64.so")
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), ctypes.c_size_t(4 << 20)) == 0
+    try:
+        big = 1 << 19  # 2 MiB of FP32
+        pb = torch.zeros(big, device=DEV)
+        mb, vb = torch.zeros(big, device=DEV), torch.zeros(big, device=DEV)
+        cst = _abi._State(1, mb.data_ptr(), vb.data_ptr(), None)
+        skip = ra.control(1.0, True)
+        rc = lib.radamw_step_inplace(pb.data_ptr(), raw.value + (3 << 20), 0, big, ctypes.byref(cst),
+                                     ctypes.byref(ra.options()), ctypes.byref(skip),
+                                     torch.cuda.current_stream().cuda_stream, ctypes.byref(upd))
+        assert rc == -1
+        rc = lib.radamw_step_inplace(pb.data_ptr(), raw.value + (2 << 20), 0, big, ctypes.byref(cst),
+                                     ctypes.byref(ra.options()), ctypes.byref(skip),
+                                     torch.cuda.current_stream().cuda_stream, ctypes.byref(upd))
+        assert rc == 0 and upd.value == 0  # exactly fits: accepted, skipped
+        upd.value = -9
+    finally:
+        torch.cuda.synchronize()
+        hip.hipFree(raw)
     # out of place: output aliasing an input
     cin = _abi._State(1, m.data_ptr(), v.data_ptr(), x.data_ptr())
     cout = _abi._State(0, buf[4 * n:].data_ptr(), v.data_ptr(), x.data_ptr())

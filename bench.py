@@ -196,7 +196,7 @@ def main(argv=None):
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
          "adamw_f32_firststep"] if args.variants == "all" else
-        [v for v in args.variants.split(",") if v != "decoder_1b"])
+        [v for v in args.variants.split(",") if v not in ("decoder_1b", "staged")])
     variants = {}
     for name in wanted:
         variant, gdt, mode = name.split("_")
@@ -245,6 +245,11 @@ def main(argv=None):
         torch.cuda.empty_cache()
 
     # --------------------------------------------------- copy ceiling --
+    # ------------------------------- staged baseline A/B (the pages' bench) --
+    staged = None
+    if args.variants == "all" or "staged" in args.variants.split(","):
+        staged = bench_staged(torch, synth, ra, dev, stream, n)
+
     # ----------------------------- tensor list: per-tensor vs one launch --
     decoder = None
     if args.variants == "all" or "decoder_1b" in args.variants.split(","):
@@ -306,11 +311,100 @@ def main(argv=None):
         "variants": variants,
         "copy_ceiling": copy_ceiling,
         "decoder_1b_list": decoder,
+        "staged_vs_fused": staged,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip},
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def bench_staged(torch, synth, ra, dev, stream, n):
+    """Fused update against the staged baseline (4 launches, 5 with AMSGrad,
+    through a delta buffer; 48 / 60 B per parameter in the pages' model).
+    (1) Device time per step on the 2^28 bucket, back-to-back launches.
+    (2) The pages' A/B shape: 65,536 elements, BF16 grads, AMSGrad, 20
+    iterations per sample x 7 samples, both variants started from the same
+    materialised state, order alternated per sample, synchronised before and
+    after every batch, wall-clock ms per step (median / min / max)."""
+    out = {}
+    for variant, bpp_f, bpp_s in (("adamw", 28, 48), ("amsgrad", 36, 60)):
+        amsgrad = variant == "amsgrad"
+        p, g, m, v, vmax = build_inputs(torch, synth, n, variant, "f32", dev)
+        delta = torch.empty_like(p)
+        o = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
+        c = ra.control(1.0)
+        res = {}
+        for name, fn in (("fused", lambda k: ra.radamw_step_inplace(p, g, ra.AdamWState(999 + k, m, v, vmax), o, c)),
+                         ("staged", lambda k: ra.radamw_step_staged_inplace(p, g, ra.AdamWState(999 + k, m, v, vmax),
+                                                                            delta, o, c))):
+            for k in range(3):
+                fn(k)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for k in range(20):
+                fn(k)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            bpp = bpp_f if name == "fused" else bpp_s
+            res[name] = {"device_ms": ms, "model_bytes_per_param": bpp, "params_per_s": n / (ms * 1e-3),
+                         "model_gbs": bpp * n / (ms * 1e-3) / 1e9}
+        res["speedup"] = res["staged"]["device_ms"] / res["fused"]["device_ms"]
+        log(f"staged vs fused, {variant} 2^28: fused {res['fused']['device_ms']:.3f} ms, staged "
+            f"{res['staged']['device_ms']:.3f} ms, x{res['speedup']:.2f}")
+        out[f"{variant}_f32_bucket"] = res
+        del p, g, m, v, vmax, delta
+        torch.cuda.empty_cache()
+
+    # the pages' A/B shape
+    small = 65536
+    key = (0, "ab-small")
+    p0 = synth.normal(small, 0.02, key + ("p",), dev)
+    g = synth.stored_grad(small, 1e-3, 128.0, "bf16", key + ("g",), dev)
+    m0, v0, x0 = synth.steady_state(small, key, True, dev)
+    o = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=True)
+    c = ra.control(128.0)
+    arms = {}
+    for name in ("fused", "staged"):
+        arms[name] = [p0.clone(), m0.clone(), v0.clone(), x0.clone(), torch.empty_like(p0)]
+
+    def run(name, k):
+        p, m, v, x, d = arms[name]
+        st = ra.AdamWState(10 + k, m, v, x)
+        if name == "fused":
+            ra.radamw_step_inplace(p, g, st, o, c)
+        else:
+            ra.radamw_step_staged_inplace(p, g, st, d, o, c)
+
+    for name in arms:  # warm both
+        for k in range(5):
+            run(name, k)
+    for name in arms:  # restart both from the same materialised state
+        for dst, src in zip(arms[name][:4], (p0, m0, v0, x0)):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    samples = {"fused": [], "staged": []}
+    for sample in range(7):
+        order = ("fused", "staged") if sample % 2 == 0 else ("staged", "fused")
+        for name in order:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(20):
+                run(name, 20 * sample + k)
+            torch.cuda.synchronize()
+            samples[name].append((time.perf_counter() - t0) * 1e3 / 20)
+    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(arms["fused"][:4], arms["staged"][:4]))
+    shape = {"elements": small, "grad_dtype": "bf16", "amsgrad": True, "iterations": 20, "samples": 7,
+             "states_bit_identical": bool(same)}
+    for name, xs in samples.items():
+        xs = sorted(xs)
+        shape[name] = {"wall_ms_per_step_median": xs[len(xs) // 2], "min": xs[0], "max": xs[-1]}
+    log(f"A/B 65,536 bf16 AMSGrad wall ms/step: fused {shape['fused']['wall_ms_per_step_median']:.4f}, staged "
+        f"{shape['staged']['wall_ms_per_step_median']:.4f}, identical states: {same}")
+    out["pages_ab_shape_65536_bf16_amsgrad"] = shape
+    return out
 
 
 def bench_decoder_list(torch, synth, ra, dev, stream):

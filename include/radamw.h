@@ -187,6 +187,23 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
                         int32_t *updated);
 
 /*
+ * The staged (unfused) baseline, for measurement only (FA-ja
+ * "割り当てとパフォーマンスのモデル", FA-zh "优化点与边界": a benchmark-only
+ * baseline of four kernels, five with AMSGrad, that re-reads the gradient
+ * and goes through a delta buffer; 48 bytes per parameter instead of 28, 60
+ * instead of 36).  Same arguments and semantics as radamw_step_inplace,
+ * plus delta: a caller-owned device scratch array of n FP32 (written).  The
+ * per-element arithmetic is the fused kernel's, split across the launches
+ * m -> v -> [v_max] -> delta -> p, so results are identical to
+ * radamw_step_inplace.  Every array must be 16-byte aligned (RADAMW_ERR_ALIGN),
+ * gradients of 16-bit types 8-byte aligned.
+ */
+int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
+                               radamw_state *st, float *delta, const radamw_options *opts,
+                               const radamw_control *ctrl, radamw_stream_t stream,
+                               int32_t *updated);
+
+/*
  * In-place update of a list of tensors that share one options struct and
  * one step count (FA-ja "サポートされている契約": a pre-flattened bucket
  * works only when every element shares the options and the step count).  A

@@ -134,6 +134,8 @@ def load(path: str = LIB_PATH):
         "radamw_step": ([vp, vp, i32, i64, P(_State), vp, P(_State), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
         "radamw_step_inplace": ([vp, vp, i32, i64, P(_State), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
         "radamw_step_multi": ([P(_Segment), i32, i32, P(u64), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
+        "radamw_step_staged_inplace": ([vp, vp, i32, i64, P(_State), vp, P(Options), P(Control), vp, P(i32)],
+                                       ctypes.c_int),
         "radamw_stats_plan": ([i64, P(i64), P(i32)], ctypes.c_int),
         "radamw_grad_stats_rows": ([i64, i32], i64),
         "radamw_grad_stats": ([vp, i32, i64, vp, i64, P(i64), vp], ctypes.c_int),
@@ -158,6 +160,7 @@ def load(path: str = LIB_PATH):
 
 
 EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "radamw_step_multi",
+           "radamw_step_staged_inplace",
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
@@ -318,6 +321,31 @@ def radamw_step_inplace(param: torch.Tensor, grad: torch.Tensor, state: AdamWSta
                                      ctypes.byref(cst), ctypes.byref(opts), ctypes.byref(ctrl),
                                      _stream(dev), ctypes.byref(updated))
     _check(rc, "radamw_step_inplace")
+    state.step = cst.step
+    return bool(updated.value)
+
+
+def radamw_step_staged_inplace(param: torch.Tensor, grad: torch.Tensor, state: AdamWState, delta: torch.Tensor,
+                               opts: Options, ctrl: Control) -> bool:
+    """The staged (unfused, 4 or 5 launches) baseline, in place; delta is an
+    FP32 scratch tensor of the same size.  For measurement."""
+    lib = load()
+    dev = param.device
+    n = param.numel()
+    _dense(param, "param", torch.float32)
+    _dense(grad, "grad", numel=n, device=dev)
+    _dense(delta, "delta", torch.float32, n, dev)
+    for name in ("exp_avg", "exp_avg_sq", "max_exp_avg_sq"):
+        t = getattr(state, name)
+        if t is not None:
+            _dense(t, f"state.{name}", torch.float32, n, dev)
+    cst = state._c()
+    updated = ctypes.c_int32(0)
+    with torch.cuda.device(dev):
+        rc = lib.radamw_step_staged_inplace(param.data_ptr(), grad.data_ptr(), _grad_code(grad), n,
+                                            ctypes.byref(cst), delta.data_ptr(), ctypes.byref(opts),
+                                            ctypes.byref(ctrl), _stream(dev), ctypes.byref(updated))
+    _check(rc, "radamw_step_staged_inplace")
     state.step = cst.step
     return bool(updated.value)
 

@@ -633,6 +633,54 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n, ra
     return multi_update(&s, 1, gdt, &st->step, *opts, ctrl->gradient_scale, dev, stream, updated);
 }
 
+int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n, radamw_state *st,
+                               float *delta, const radamw_options *opts, const radamw_control *ctrl,
+                               radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!valid_dtype(gdt) || n < 0 || !st || !updated) return RADAMW_ERR_INVALID;
+    if (st->step == UINT64_MAX) return RADAMW_ERR_STATE;
+    const bool ams = opts->amsgrad != 0;
+    if (n == 0) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    if ((st->max_exp_avg_sq != nullptr) != ams) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    const int64_t fb = n * 4, gb = n * static_cast<int64_t>(grad_bytes(gdt));
+    PtrChecker pc(dev);
+    // every stream is read in 16-byte chunks (8-byte for 16-bit gradients)
+    if ((rc = pc.check(p, 16, fb)) || (rc = pc.check(g, 4 * grad_bytes(gdt), gb)) ||
+        (rc = pc.check(st->exp_avg, 16, fb)) || (rc = pc.check(st->exp_avg_sq, 16, fb)) ||
+        (rc = pc.check(delta, 16, fb)) || (ams && (rc = pc.check(st->max_exp_avg_sq, 16, fb))))
+        return rc;
+    std::vector<Range> ranges;
+    add_range(ranges, g, gb, false);
+    add_range(ranges, p, fb, true);
+    add_range(ranges, st->exp_avg, fb, true);
+    add_range(ranges, st->exp_avg_sq, fb, true);
+    add_range(ranges, delta, fb, true);
+    if (ams) add_range(ranges, st->max_exp_avg_sq, fb, true);
+    if ((rc = check_alias(ranges))) return rc;
+    if ((n >> 2) + (n & 3) > UPDATE_MAX_GRID * 64) return RADAMW_ERR_RANGE;
+    if (ctrl->skip_update) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    const Coefs c = make_coefs(*opts, st->step + 1, ctrl->gradient_scale);
+    int launched = 0;
+    hipError_t e = launch_staged(p, g, gdt, st->exp_avg, st->exp_avg_sq, ams ? st->max_exp_avg_sq : nullptr,
+                                 delta, n, st->step == 0, c, stream, &launched);
+    g_launches.fetch_add(static_cast<uint64_t>(launched), std::memory_order_relaxed);
+    if (e != hipSuccess) return hip_status(e);
+    st->step += 1;
+    *updated = 1;
+    return RADAMW_OK;
+}
+
 int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, uint64_t *step,
                       const radamw_options *opts, const radamw_control *ctrl,
                       radamw_stream_t stream_, int32_t *updated) {

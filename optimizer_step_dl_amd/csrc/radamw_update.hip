@@ -20,7 +20,7 @@
 // Each workgroup is a single wave64 that handles one tile and exits, so the
 // dispatcher keeps the whole chip full of short, independent request
 // streams.  No MFMA: there is no contraction here.
-#include "radamw_internal.h"
+#include "radamw_math.h"
 
 #include <hip/hip_ext.h>
 
@@ -90,29 +90,21 @@ __device__ __forceinline__ float load_grad1(const void *g, int64_t e) {
     }
 }
 
-// The per-element update (FA-ja "この演算子を使用する理由").  Division by
-// the bias corrections is done with host-formed reciprocals (lr / bc1 and
-// 1 / bc2) and the final division with v_rcp_f32; the square root is
-// v_sqrt_f32.  Each differs from the correctly rounded FP32 operation by at
-// most about one ulp, which the pages allow (device math is FP32 and may be
-// fused or reassociated; results are compared with a tolerance).
+// The per-element update (FA-ja "この演算子を使用する理由"), built from the
+// shared helpers of radamw_math.h.  FIRST starts the moments from zero
+// without reading them.
 template <bool AMS, bool FIRST>
 __device__ __forceinline__ void adamw_element(float x, float &p, float &m, float &v, float &vmax,
                                               const Coefs &c) {
-    const float g = x * c.inv_scale;
-    const float m_old = FIRST ? 0.0f : m;
-    const float v_old = FIRST ? 0.0f : v;
-    m = c.beta1 * m_old + c.one_minus_beta1 * g;
-    v = c.beta2 * v_old + (c.one_minus_beta2 * g) * g;
+    const float g = unscale(x, c);
+    m = first_moment(FIRST ? 0.0f : m, g, c);
+    v = second_moment(FIRST ? 0.0f : v, g, c);
     float v_used = v;
     if constexpr (AMS) {
-        const float vmax_old = FIRST ? 0.0f : vmax;
-        v_used = fmaxf(vmax_old, v);
+        v_used = fmaxf(FIRST ? 0.0f : vmax, v);
         vmax = v_used;
     }
-    const float denom = __builtin_amdgcn_sqrtf(v_used * c.inv_bc2) + c.eps;
-    const float update = (c.step_size * m) * __builtin_amdgcn_rcpf(denom);
-    p = p * c.decay - update;
+    p = apply_step(p, step_delta(m, v_used, c), c);
 }
 
 template <int GDT, bool AMS, bool FIRST>

@@ -407,3 +407,42 @@ def test_rejections_leave_everything_untouched():
     assert upd.value == -9
     assert ra.radamw_launch_count() == launches
     assert unchanged(before, [buf])
+
+
+# ------------------------------------------------------- staged baseline --
+
+@pytest.mark.parametrize("gdt,amsgrad", [("f32", False), ("f32", True), ("bf16", True), ("f16", False)])
+def test_staged_baseline_is_bit_identical_to_fused(gdt, amsgrad):
+    """The staged baseline (4 launches, 5 with AMSGrad, through a delta
+    buffer) runs the fused kernel's per-element arithmetic split across
+    launches: bit-identical results, and both within the oracle bar."""
+    n = 3 * 1024 + 7
+    announce(f"staged {gdt} ams={amsgrad}")
+    opts = ra.options(lr=1e-2, beta1=0.8, beta2=0.95, eps=1e-3, weight_decay=0.1, amsgrad=amsgrad)
+    p0 = synth.normal(n, 0.02, (0, "staged", gdt, "p"))
+    pf, sf = p0.to(DEV), new_gpu_state(n, amsgrad)
+    ps, ss = p0.to(DEV), new_gpu_state(n, amsgrad)
+    delta = torch.empty(n, device=DEV)
+    p_ref, st_ref = p0.numpy().copy(), oracle.State(n, amsgrad)
+    for t in range(1, 4):
+        g = synth.stored_grad(n, 1e-3, 64.0, gdt, (0, "staged", gdt, "g", t))
+        gd = g.to(DEV)
+        assert ra.radamw_step_inplace(pf, gd, sf, opts, ra.control(64.0))
+        before = ra.radamw_launch_count()
+        assert ra.radamw_step_staged_inplace(ps, gd, ss, delta, opts, ra.control(64.0))
+        assert ra.radamw_launch_count() == before + (5 if amsgrad else 4)
+        oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts), 64.0)
+        torch.cuda.synchronize()
+        assert ss.step == sf.step == t
+        assert bits_equal(ps, pf) and bits_equal(ss.exp_avg, sf.exp_avg) and bits_equal(ss.exp_avg_sq, sf.exp_avg_sq)
+        if amsgrad:
+            assert bits_equal(ss.max_exp_avg_sq, sf.max_exp_avg_sq)
+        _compare_state(ps, ss, p_ref, st_ref, amsgrad, f"staged t={t}", one_step=True)
+    # skip launches nothing; misaligned arrays are rejected
+    before = ra.radamw_launch_count()
+    assert not ra.radamw_step_staged_inplace(ps, gd, ss, delta, opts, ra.control(64.0, True))
+    assert ra.radamw_launch_count() == before and ss.step == 3
+    buf = torch.zeros(n + 1, device=DEV)
+    with pytest.raises(ra.RadamwError) as e:
+        ra.radamw_step_staged_inplace(buf[1:], gd, ss, delta, opts, ra.control(64.0))
+    assert e.value.status == -4

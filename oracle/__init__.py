@@ -79,6 +79,8 @@ def _load():
     lib.oracle_stats_plan.restype = i32
     lib.oracle_clip_coefficient.argtypes = [ctypes.c_double] * 3
     lib.oracle_clip_coefficient.restype = ctypes.c_double
+    lib.oracle_round_copy.argtypes = [vp, i64, i32, vp]
+    lib.oracle_round_copy.restype = None
     _lib = lib
     return lib
 
@@ -220,3 +222,13 @@ def decide(sumsq: float, nonfinite: int, gradient_scale: float, max_norm: float 
     if nonfinite > 0:
         return True, gradient_scale
     return False, gradient_scale / clip_coefficient(sumsq, gradient_scale, max_norm)
+
+
+def round_copy(p: np.ndarray, dtype) -> np.ndarray:
+    """The FP16 / BF16 model copy of FP32 values (raw uint16 bits), rounded to
+    nearest even (the FP32-master write-back)."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    assert code in (F16, BF16) and p.dtype == np.float32 and p.flags["C_CONTIGUOUS"]
+    out = np.empty(p.size, np.uint16)
+    _load().oracle_round_copy(_ptr(p), p.size, code, _ptr(out))
+    return out

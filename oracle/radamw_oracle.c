@@ -249,3 +249,62 @@ double oracle_clip_coefficient(double sumsq, double gradient_scale,
     double coef = max_norm / (norm + 1e-6);
     return coef < 1.0 ? coef : 1.0;
 }
+
+/*
+ * Low-precision copy of the updated FP32 master parameters (the model copy
+ * an FP32-master optimizer maintains; TR-zh "训练与状态保存": FP32 master
+ * parameters, FP16 / BF16 model storage).  Round to nearest, ties to even,
+ * written out from the two formats' definitions.
+ */
+
+/* bfloat16: keep the upper 16 bits of the binary32 encoding, rounding on the
+ * lower 16 (ties to the even upper half); a NaN stays a (quiet) NaN. */
+uint16_t oracle_round_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return (uint16_t)((u >> 16) | 0x0040);
+    uint32_t upper = u >> 16;
+    uint32_t lower = u & 0xffffu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1; /* a carry into the exponent is the correct next value */
+    return (uint16_t)upper;
+}
+
+/* IEEE binary16: the representable values near |x| are multiples of the
+ * quantum 2^(E-10) for a normal binade [2^E, 2^(E+1)) and 2^-24 below 2^-14;
+ * round |x| to the nearest multiple (ties to even, rint in the default
+ * rounding mode), saturate to infinity above 65504, then encode. */
+uint16_t oracle_round_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return sign | 0x7e00;
+    double a = fabs((double)x);
+    if (isinf(a))
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1): binade exponent e2 - 1 */
+    int binade = e2 - 1;
+    int qexp = binade < -14 ? -24 : binade - 10;
+    double q = rint(ldexp(a, -qexp)); /* quanta, exact integer */
+    double v = ldexp(q, qexp);        /* the rounded magnitude */
+    if (v > 65504.0)
+        return sign | 0x7c00;
+    if (qexp == -24)
+        return sign | (uint16_t)q; /* subnormal count; q == 1024 encodes 2^-14 */
+    frexp(v, &e2);
+    binade = e2 - 1; /* may have moved up one binade by rounding */
+    uint16_t mant = (uint16_t)(ldexp(v, 10 - binade) - 1024.0);
+    return sign | (uint16_t)((binade + 15) << 10) | mant;
+}
+
+/* Round n FP32 values to the copy's dtype (ORACLE_F16 or ORACLE_BF16). */
+void oracle_round_copy(const float *p, int64_t n, int32_t dtype, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dtype == ORACLE_F16 ? oracle_round_f16(p[i]) : oracle_round_bf16(p[i]);
+}

@@ -460,3 +460,41 @@ def test_clip_decision_matches_torch_clip_grad_norm():
     assert eff2 == scale and not skip
     assert oracle.decide(sumsq, 3, scale, max_norm) == (True, scale)
     assert oracle.decide(sumsq, 0, scale, None) == (False, scale)
+
+
+# ------------------------------------------------ low-precision write-back --
+
+def _rounding_probe_values():
+    rng = np.random.Generator(np.random.PCG64(7))
+    parts = [
+        rng.standard_normal(200_000).astype(np.float32) * np.float32(0.02),
+        (rng.standard_normal(100_000) * 1e4).astype(np.float32),
+        np.exp(rng.uniform(-120, 88, 100_000)).astype(np.float32) * rng.choice([-1, 1], 100_000).astype(np.float32),
+        rng.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32).view(np.float32),  # every bit pattern class
+        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 65519.99, 65520.0, 2.0**-24, 2.0**-25,
+                  2.0**-25 * 1.0000001, 3 * 2.0**-26, 2.0**-14, 2.0**-14 * (1 - 2.0**-11), 1.0 + 2.0**-11,
+                  1.0 + 3 * 2.0**-11, 3.4028235e38, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8], np.float32),
+    ]
+    # exact ties for both formats
+    base = rng.standard_normal(50_000).astype(np.float32).view(np.uint32)
+    parts.append(((base & ~np.uint32(0xFFFF)) | np.uint32(0x8000)).view(np.float32))
+    parts.append(((base & ~np.uint32(0x1FFF)) | np.uint32(0x1000)).view(np.float32))
+    return np.concatenate(parts)
+
+
+def test_f16_rounding_matches_numpy():
+    x = _rounding_probe_values()
+    ours = oracle.round_copy(x, "f16")
+    ref = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.all(np.isnan(ours[nan].view(np.float16)))
+
+
+def test_bf16_rounding_matches_torch():
+    x = _rounding_probe_values()
+    ours = oracle.round_copy(x, "bf16")
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.all(np.isnan(torch.from_numpy(ours[nan].view(np.int16)).view(torch.bfloat16).float().numpy()))

@@ -40,6 +40,7 @@ BYTES_PER_PARAM = {  # algorithmic bytes moved per element by one update
     ("adamw", "f32", False): 28, ("adamw", "bf16", False): 26, ("adamw", "f16", False): 26,
     ("amsgrad", "f32", False): 36, ("amsgrad", "bf16", False): 34, ("amsgrad", "f16", False): 34,
     ("adamw", "f32", True): 20, ("amsgrad", "f32", True): 24,
+    ("adamw", "f32", "bf16copy"): 30,
 }
 PROFILE_COUNTERS = os.path.join(HERE, "profiles", "update_adamw_f32_268M_counters.md")
 KERNEL_SOURCES = [os.path.join(HERE, "optimizer_step_dl_amd", "csrc", f)
@@ -195,7 +196,7 @@ def main(argv=None):
     # ------------------------------------------------ update-only variants --
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
-         "adamw_f32_firststep"] if args.variants == "all" else
+         "adamw_f32_firststep", "adamw_f32_bf16copy"] if args.variants == "all" else
         [v for v in args.variants.split(",") if v not in ("decoder_1b", "staged")])
     variants = {}
     for name in wanted:
@@ -206,7 +207,14 @@ def main(argv=None):
         o = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
         c = ra.control(1.0)
         st_step = 0 if first else 999
-        if mode == "outofplace":
+        if mode == "bf16copy":
+            # in place, plus the BF16 model copy written in the same pass
+            model = torch.empty(n, dtype=torch.bfloat16, device=dev)
+            seg = [ra.Segment(p, g, m, v, vmax)]
+
+            def launch(k):
+                ra.radamw_step_multi_writeback(seg, [model], st_step + k, o, c)
+        elif mode == "outofplace":
             outs = [torch.empty_like(p), torch.empty_like(m), torch.empty_like(v),
                     torch.empty_like(vmax) if amsgrad else None]
             sets = [(p, m, v, vmax), tuple(outs)]
@@ -234,7 +242,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in ev]
         avg = sum(ms) / len(ms)
-        bp = BYTES_PER_PARAM[(variant, gdt, first)]
+        bp = BYTES_PER_PARAM[(variant, gdt, "bf16copy" if mode == "bf16copy" else first)]
         variants[name] = {"avg_ms": avg, "min_ms": min(ms), "bytes_per_param": bp,
                           "params_per_s": n / (avg * 1e-3), "gbs": bp * n / (avg * 1e-3) / 1e9,
                           "frac_of_peak": bp * n / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}

@@ -225,6 +225,22 @@ int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt
                       int32_t *updated);
 
 /*
+ * radamw_step_multi that also writes a 16-bit model copy of the updated
+ * parameters in the same pass: models[i] (device, segs[i].n elements of
+ * model_dtype, written) receives segs[i].param after the update, rounded to
+ * nearest even (the FP16 / BF16 model weights of an FP32-master optimizer,
+ * TR-zh "训练与状态保存": FP32 master parameters, 16-bit model storage).
+ * models[i] may be NULL (no copy for that tensor).  model_dtype is
+ * RADAMW_F16 or RADAMW_BF16.  Adds 2 bytes per parameter of traffic; the
+ * update itself is identical to radamw_step_multi's.  Copies may overlap
+ * nothing (RADAMW_ERR_ALIAS).
+ */
+int radamw_step_multi_writeback(const radamw_segment *segs, void *const *models, int32_t nseg,
+                                radamw_dtype gdt, radamw_dtype model_dtype, uint64_t *step,
+                                const radamw_options *opts, const radamw_control *ctrl,
+                                radamw_stream_t stream, int32_t *updated);
+
+/*
  * Merge plan for rows statistics records (FA-ja "ネイティブ PyTorch
  * ストレージと階層統計": StatsPlan; TR-zh "在 ruda:0 上进行原生 PyTorch
  * 训练": fan-in 1024, at most two extra merge kernels, at most 49,200 bytes

@@ -136,6 +136,8 @@ def load(path: str = LIB_PATH):
         "radamw_step_multi": ([P(_Segment), i32, i32, P(u64), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
         "radamw_step_staged_inplace": ([vp, vp, i32, i64, P(_State), vp, P(Options), P(Control), vp, P(i32)],
                                        ctypes.c_int),
+        "radamw_step_multi_writeback": ([P(_Segment), P(vp), i32, i32, i32, P(u64), P(Options), P(Control), vp,
+                                         P(i32)], ctypes.c_int),
         "radamw_stats_plan": ([i64, P(i64), P(i32)], ctypes.c_int),
         "radamw_grad_stats_rows": ([i64, i32], i64),
         "radamw_grad_stats": ([vp, i32, i64, vp, i64, P(i64), vp], ctypes.c_int),
@@ -160,7 +162,7 @@ def load(path: str = LIB_PATH):
 
 
 EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "radamw_step_multi",
-           "radamw_step_staged_inplace",
+           "radamw_step_staged_inplace", "radamw_step_multi_writeback",
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
@@ -361,6 +363,36 @@ def radamw_step_multi(segments, step: int, opts: Options, ctrl: Control):
         rc = lib.radamw_step_multi(arr, count, code, ctypes.byref(st), ctypes.byref(opts),
                                    ctypes.byref(ctrl), _stream(dev), ctypes.byref(updated))
     _check(rc, "radamw_step_multi")
+    return bool(updated.value), int(st.value)
+
+
+def radamw_step_multi_writeback(segments, models: Sequence[Optional[torch.Tensor]], step: int, opts: Options,
+                                ctrl: Control):
+    """radamw_step_multi plus a 16-bit model copy per tensor, written in the
+    same pass.  models[i] is a float16 / bfloat16 tensor of segments[i]'s
+    size, or None; all copies share one dtype.  Returns (updated, new_step)."""
+    lib = load()
+    arr, code, dev, count = _marshal(segments)
+    if len(models) != count:
+        raise ValueError("one model entry (tensor or None) per segment")
+    segs = segments.segments if isinstance(segments, SegmentList) else segments
+    mdt = None
+    ptrs = (ctypes.c_void_p * max(1, count))()
+    for i, (m, s) in enumerate(zip(models, segs)):
+        if m is None:
+            continue
+        _dense(m, f"model copy {i}", numel=s.param.numel(), device=dev)
+        if m.dtype not in (torch.float16, torch.bfloat16) or (mdt is not None and m.dtype != mdt):
+            raise ValueError("model copies must all be float16 or all bfloat16")
+        mdt = m.dtype
+        ptrs[i] = m.data_ptr()
+    st = ctypes.c_uint64(step)
+    updated = ctypes.c_int32(0)
+    with torch.cuda.device(dev):
+        rc = lib.radamw_step_multi_writeback(arr, ptrs, count, code, _DTYPE_CODE[mdt or torch.bfloat16],
+                                             ctypes.byref(st), ctypes.byref(opts), ctypes.byref(ctrl), _stream(dev),
+                                             ctypes.byref(updated))
+    _check(rc, "radamw_step_multi_writeback")
     return bool(updated.value), int(st.value)
 
 

@@ -229,6 +229,10 @@ int32_t segment_head(const SegDesc &s, int gdt, bool amsgrad, bool first) {
     const uintptr_t ga = reinterpret_cast<uintptr_t>(s.g);
     const int gphase = gdt == RADAMW_F32 ? static_cast<int>((ga >> 2) & 3) : static_cast<int>((ga >> 1) & 3);
     ok = ok && gphase == phase;
+    if (s.model_kind) {
+        const uintptr_t ma = reinterpret_cast<uintptr_t>(s.model);
+        ok = ok && (ma & 1) == 0 && static_cast<int>((ma >> 1) & 3) == phase;
+    }
     if (!ok) return -1;
     int64_t head = (4 - phase) & 3;
     if (head > s.n) head = s.n;
@@ -375,10 +379,12 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     return RADAMW_OK;
 }
 
-// Validated multi-tensor update (shared by radamw_step_multi and the fused step).
+// Validated multi-tensor update (shared by radamw_step_multi, the write-back
+// variant and the fused step).  models (optional) holds a 16-bit model copy
+// per segment (entries may be null), of dtype model_dtype.
 int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *step,
                  const radamw_options &o, double gradient_scale, int dev, hipStream_t stream,
-                 int32_t *updated) {
+                 int32_t *updated, void *const *models = nullptr, int model_dtype = 0) {
     std::vector<SegDesc> active;
     active.reserve(nseg);
     const bool first = (*step == 0);
@@ -396,6 +402,10 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
         d.v_out = s.exp_avg_sq;
         d.vmax_out = s.max_exp_avg_sq;
         d.n = s.n;
+        if (models && models[i]) {
+            d.model = models[i];
+            d.model_kind = model_dtype == RADAMW_BF16 ? G_BF16 : G_F16;
+        }
         active.push_back(d);
     }
     if (active.empty()) {
@@ -428,9 +438,10 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
     return RADAMW_OK;
 }
 
-// Validate a segment list for an in-place multi-tensor update.
+// Validate a segment list for an in-place multi-tensor update (and its
+// optional 16-bit model copies, which are written ranges too).
 int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgrad, bool first,
-                   int dev, int64_t *active_out) {
+                   int dev, int64_t *active_out, void *const *models = nullptr) {
     if (nseg < 0 || (nseg > 0 && !segs)) return RADAMW_ERR_INVALID;
     PtrChecker pc(dev);
     std::vector<Range> ranges;
@@ -451,6 +462,10 @@ int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgr
         d.n = s.n;
         int rc = check_update_tensor(d, gdt, amsgrad, first, true, pc, ranges);
         if (rc) return rc;
+        if (models && models[i]) {
+            if ((rc = pc.check(models[i], 2, s.n * 2))) return rc;
+            add_range(ranges, models[i], s.n * 2, true);
+        }
     }
     if (active_out) *active_out = active;
     return check_alias(ranges);
@@ -699,6 +714,30 @@ int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt
         return RADAMW_OK;
     }
     return multi_update(segs, nseg, gdt, step, *opts, ctrl->gradient_scale, dev, stream, updated);
+}
+
+int radamw_step_multi_writeback(const radamw_segment *segs, void *const *models, int32_t nseg,
+                                radamw_dtype gdt, radamw_dtype model_dtype, uint64_t *step,
+                                const radamw_options *opts, const radamw_control *ctrl,
+                                radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!valid_dtype(gdt) || !step || !updated) return RADAMW_ERR_INVALID;
+    if (model_dtype != RADAMW_F16 && model_dtype != RADAMW_BF16) return RADAMW_ERR_INVALID;
+    if (nseg > 0 && !models) return RADAMW_ERR_INVALID;
+    if (*step == UINT64_MAX) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    int64_t active = 0;
+    if ((rc = check_segments(segs, nseg, gdt, opts->amsgrad != 0, *step == 0, dev, &active, models))) return rc;
+    if (ctrl->skip_update || active == 0) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    return multi_update(segs, nseg, gdt, step, *opts, ctrl->gradient_scale, dev, stream, updated, models,
+                        model_dtype);
 }
 
 int radamw_stats_plan(int64_t rows, int64_t *scratch_elements, int32_t *extra_merge_kernels) {

@@ -67,7 +67,9 @@ struct Coefs {
 // *_out pointers equal the *_in pointers.  head is the number of leading
 // elements handled by scalar code so that every stream is 16-byte aligned
 // from element `head` on (0..3); head == -1 marks a segment whose streams
-// are not mutually aligned, processed entirely by scalar code.
+// are not mutually aligned, processed entirely by scalar code.  model, when
+// model_kind is G_F16 or G_BF16, receives the updated parameters rounded to
+// that 16-bit type (the model copy of an FP32-master optimizer).
 struct SegDesc {
     const float *p_in;
     const void *g;
@@ -78,10 +80,11 @@ struct SegDesc {
     float *m_out;
     float *v_out;
     float *vmax_out;
+    void *model;
     int64_t n;
     int64_t tile_begin;  // first tile of this segment in the launch's tile space
     int32_t head;
-    int32_t pad;
+    int32_t model_kind;  // 0: no copy; G_F16 / G_BF16: copy dtype
 };
 
 // Tiles a segment occupies (0 for an empty segment).

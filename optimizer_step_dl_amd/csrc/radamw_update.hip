@@ -29,6 +29,7 @@ namespace radamw {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 #ifndef RADAMW_NT_LOADS
 #define RADAMW_NT_LOADS 1
@@ -119,6 +120,8 @@ __device__ __forceinline__ void scalar_element(const SegDesc &s, int64_t e, cons
     }
     adamw_element<AMS, FIRST>(x, p, m, v, vmax, c);
     gl(s.p_out)[e] = p;
+    if (s.model_kind == G_BF16) gl(static_cast<__bf16 *>(s.model))[e] = static_cast<__bf16>(p);
+    else if (s.model_kind == G_F16) gl(static_cast<_Float16 *>(s.model))[e] = static_cast<_Float16>(p);
     gl(s.m_out)[e] = m;
     gl(s.v_out)[e] = v;
     if constexpr (AMS) gl(s.vmax_out)[e] = vmax;
@@ -143,6 +146,16 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
     f32x4 *m_out = reinterpret_cast<f32x4 *>(s.m_out + head);
     f32x4 *v_out = reinterpret_cast<f32x4 *>(s.v_out + head);
     f32x4 *x_out = reinterpret_cast<f32x4 *>(s.vmax_out + head);
+
+    // the model copy (round to nearest even: v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32)
+    auto store_copy = [&](int64_t k, const f32x4 &P) {
+        if (s.model_kind == G_BF16)
+            stream_store(reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(s.model) + head) + k,
+                         __builtin_convertvector(P, bf16x4));
+        else if (s.model_kind == G_F16)
+            stream_store(reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(s.model) + head) + k,
+                         __builtin_convertvector(P, f16x4));
+    };
 
     auto chunk = [&](f32x4 G, f32x4 &P, f32x4 &M, f32x4 &V, f32x4 &X) {
 #pragma unroll
@@ -173,6 +186,7 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
             const int64_t k = base + int64_t(u) * UPDATE_BLOCK + tid;
             chunk(G[u], P[u], M[u], V[u], X[u]);
             stream_store(p_out + k, P[u]);
+            store_copy(k, P[u]);
             stream_store(m_out + k, M[u]);
             stream_store(v_out + k, V[u]);
             if constexpr (AMS) stream_store(x_out + k, X[u]);
@@ -192,6 +206,7 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
                 }
                 chunk(G, P, M, V, X);
                 stream_store(p_out + k, P);
+                store_copy(k, P);
                 stream_store(m_out + k, M);
                 stream_store(v_out + k, V);
                 if constexpr (AMS) stream_store(x_out + k, X);

@@ -14,7 +14,10 @@ Behaviour (TR-zh):
     the unscaled gradients of all active groups and requires
     ``fused_step=True``.  Both booleans default to False, clipping to None.
   * ``.grad`` is kept (the caller clears it before the next accumulation
-    window); master parameters and moments are FP32.
+    window); master parameters and moments are FP32.  ``model_copies`` maps
+    master parameters to float16 / bfloat16 model tensors that the update
+    rewrites in the same pass (the low-precision write-back an FP32-master
+    optimizer performs).
   * ``state_dict()`` records the step options; with hierarchical statistics
     the options carry version 2.  An archive without step options restores
     with the fused and hierarchical modes off.
@@ -41,7 +44,7 @@ class FusedAdamW(torch.optim.Optimizer):
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-5,
                  weight_decay: float = 1e-4, amsgrad: bool = False, *, maximize: bool = False,
                  fused_step: bool = False, max_grad_norm: Optional[float] = None,
-                 hierarchical_stats: bool = False):
+                 hierarchical_stats: bool = False, model_copies: Optional[dict] = None):
         if max_grad_norm is not None and not fused_step:
             raise ValueError("max_grad_norm requires fused_step=True")
         if max_grad_norm is not None and not (math.isfinite(max_grad_norm) and max_grad_norm > 0):
@@ -54,6 +57,16 @@ class FusedAdamW(torch.optim.Optimizer):
         self.hierarchical_stats = bool(hierarchical_stats)
         self._workspace: Optional[torch.Tensor] = None
         self.last_result: Optional[_abi.FusedResult] = None
+        self._copies: dict = {}
+        for master, copy in (model_copies or {}).items():
+            self.attach_model_copy(master, copy)
+
+    def attach_model_copy(self, master: torch.Tensor, copy: torch.Tensor) -> None:
+        """Keep a float16 / bfloat16 model copy of an FP32 master parameter:
+        every update rewrites it (rounded to nearest even) in the same pass."""
+        if copy.dtype not in (torch.float16, torch.bfloat16) or copy.shape != master.shape:
+            raise ValueError("a model copy is a float16 / bfloat16 tensor of the master's shape")
+        self._copies[master] = copy
 
     # ------------------------------------------------------------ state --
     def _state_for(self, p: torch.Tensor, amsgrad: bool):
@@ -116,12 +129,18 @@ class FusedAdamW(torch.optim.Optimizer):
                 return loss  # whole step skipped: non-finite gradient
         for group, items in active:
             opts = self._options(group)
-            by_step = {}
+            by_step = {}  # one launch set per (step count, model-copy dtype)
             for p, st in items:
-                by_step.setdefault(st["step"], []).append((p, st))
-            for step, members in by_step.items():
+                copy = self._copies.get(p)
+                key = (st["step"], None if copy is None else copy.dtype)
+                by_step.setdefault(key, []).append((p, st))
+            for (step, copy_dtype), members in by_step.items():
                 segs = [self._segment(p, st) for p, st in members]
-                _, new_step = _abi.radamw_step_multi(segs, step, opts, ctrl)
+                if copy_dtype is None:
+                    _, new_step = _abi.radamw_step_multi(segs, step, opts, ctrl)
+                else:
+                    copies = [self._copies[p] for p, _ in members]
+                    _, new_step = _abi.radamw_step_multi_writeback(segs, copies, step, opts, ctrl)
                 for _, st in members:
                     st["step"] = new_step
         return loss

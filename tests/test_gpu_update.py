@@ -446,3 +446,64 @@ def test_staged_baseline_is_bit_identical_to_fused(gdt, amsgrad):
     with pytest.raises(ra.RadamwError) as e:
         ra.radamw_step_staged_inplace(buf[1:], gd, ss, delta, opts, ra.control(64.0))
     assert e.value.status == -4
+
+
+# ------------------------------------------------- low-precision write-back --
+
+@pytest.mark.parametrize("copy_dtype", [torch.bfloat16, torch.float16])
+def test_writeback_copy_is_the_rounded_update(copy_dtype):
+    """radamw_step_multi_writeback: the update itself is bit-identical to
+    radamw_step_multi; each model copy equals torch's round-to-nearest-even
+    conversion of the updated FP32 parameters bit for bit, and the oracle's
+    rounded parameters within one unit of the 16-bit format."""
+    sizes = [5, 4096, 4099, 70001, 1 << 22]  # the largest takes a launch of its own
+    announce(f"write-back {copy_dtype}")
+    opts = ra.options(lr=1e-2, weight_decay=0.1, amsgrad=True)
+    segs, twins, copies, refs = [], [], [], []
+    for i, n in enumerate(sizes):
+        p0 = synth.normal(n, 0.02, (0, "wb", i, "p"))
+        g = synth.stored_grad(n, 1e-3, 1.0, "bf16", (0, "wb", i, "g")).to(DEV)
+        for dst in (segs, twins):
+            st = new_gpu_state(n, True)
+            dst.append(ra.Segment(p0.to(DEV), g, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq))
+        copies.append(None if i == 0 else torch.full((n,), 7.0, dtype=copy_dtype, device=DEV))
+        refs.append((p0.numpy().copy(), oracle.State(n, True), grad_host(g)))
+    step = 0
+    for t in (1, 2):
+        _, step = ra.radamw_step_multi_writeback(segs, copies, step, opts, ra.control())
+        ra.radamw_step_multi(twins, t - 1, opts, ra.control())
+        for p_ref, st_ref, gh in refs:
+            oracle.adamw_step(p_ref, gh, "bf16", st_ref, oracle_opts(opts))
+    torch.cuda.synchronize()
+    name = "f16" if copy_dtype == torch.float16 else "bf16"
+    for i, (s, tw, cp) in enumerate(zip(segs, twins, copies)):
+        assert bits_equal(s.param, tw.param) and bits_equal(s.max_exp_avg_sq, tw.max_exp_avg_sq)
+        if cp is None:
+            continue
+        assert torch.equal(cp.view(torch.int16), s.param.to(copy_dtype).view(torch.int16)), f"segment {i}"
+        # against the oracle: the copies differ by at most the FP32 contract
+        # bound on p plus one unit of the 16-bit format (values, not
+        # encodings: near p = 0 the FP32 discrepancy of a few ulps of the
+        # update spans many 16-bit ulps of p)
+        ours = cp.float().cpu().numpy().astype(np.float64)
+        ref_bits = oracle.round_copy(refs[i][0], name)
+        ref = (torch.from_numpy(ref_bits.view(np.int16)).view(copy_dtype).double().numpy())
+        unit = 2.0 ** (-7 if copy_dtype == torch.bfloat16 else -10)
+        p_ref = refs[i][0].astype(np.float64)
+        assert np.all(np.abs(ours - ref) <= 1e-6 * (1 + np.abs(p_ref)) + unit * np.abs(p_ref) + 2.0**-24), f"segment {i}"
+        assert np.mean(ours == ref) > 0.99
+
+
+def test_fused_adamw_keeps_model_copies():
+    from optimizer_step_dl_amd.optim import FusedAdamW
+    announce("FusedAdamW model copies")
+    params = [torch.nn.Parameter(synth.normal(n, 0.02, (0, "fwb", n)).to(DEV)) for n in (1000, 33333)]
+    copies = {p: p.detach().to(torch.bfloat16) for p in params}
+    opt = FusedAdamW(params, lr=1e-2, model_copies=copies)
+    for t in range(3):
+        for p in params:
+            p.grad = synth.stored_grad(p.numel(), 1e-3, 1.0, "f32", (0, "fwb", p.numel(), t)).to(DEV)
+        opt.step()
+    torch.cuda.synchronize()
+    for p in params:
+        assert torch.equal(copies[p].view(torch.int16), p.detach().to(torch.bfloat16).view(torch.int16))

@@ -66,7 +66,8 @@ def counters_from_profile():
     absent or taken on a different kernel source."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
-    text = open(PROFILE_COUNTERS).read()
+    with open(PROFILE_COUNTERS) as f:
+        text = f.read()
     vals = dict(re.findall(r"^- ([a-z_0-9]+): ([0-9A-Za-z.+\-e]+)\s*$", text, flags=re.M))
     try:
         if vals.get("kernel_source_sha256_16") != kernel_source_hash():

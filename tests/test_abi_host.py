@@ -27,7 +27,8 @@ def lib():
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "radamw.h")).read()
+    with open(os.path.join(ROOT, "include", "radamw.h")) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(radamw_[a-z0-9_]+)\s*\(", text))
 

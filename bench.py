@@ -44,7 +44,7 @@ BYTES_PER_PARAM = {  # algorithmic bytes moved per element by one update
 }
 PROFILE_COUNTERS = os.path.join(HERE, "profiles", "update_adamw_f32_268M_counters.md")
 KERNEL_SOURCES = [os.path.join(HERE, "optimizer_step_dl_amd", "csrc", f)
-                  for f in ("radamw_update.hip", "radamw_internal.h")]
+                  for f in ("radamw_update.hip", "radamw_math.h", "radamw_internal.h")]
 
 
 def log(msg):

@@ -198,7 +198,7 @@ def main(argv=None):
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
          "adamw_f32_firststep", "adamw_f32_bf16copy"] if args.variants == "all" else
-        [v for v in args.variants.split(",") if v not in ("decoder_1b", "staged")])
+        [v for v in args.variants.split(",") if v not in ("decoder_1b", "decoder_7b", "staged")])
     variants = {}
     for name in wanted:
         variant, gdt, mode = name.split("_")
@@ -264,6 +264,11 @@ def main(argv=None):
     if args.variants == "all" or "decoder_1b" in args.variants.split(","):
         decoder = bench_decoder_list(torch, synth, ra, dev, stream)
 
+    # ------------------ the 6.7B-parameter list: whole fused step at scale --
+    decoder7 = None
+    if args.variants == "all" or "decoder_7b" in args.variants.split(","):
+        decoder7 = bench_decoder_7b(torch, synth, ra, dev, stream)
+
     # A plain elementwise copy of known size (1 GiB read, 1 GiB written):
     # torch's unary negation kernel.  It is the calibration kernel for the
     # rocprofv3 HBM counters and, timed, a context ceiling for streaming.
@@ -321,6 +326,7 @@ def main(argv=None):
         "copy_ceiling": copy_ceiling,
         "decoder_1b_list": decoder,
         "staged_vs_fused": staged,
+        "decoder_7b_fused_step": decoder7,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip},
     }
@@ -413,6 +419,50 @@ def bench_staged(torch, synth, ra, dev, stream, n):
     log(f"A/B 65,536 bf16 AMSGrad wall ms/step: fused {shape['fused']['wall_ms_per_step_median']:.4f}, staged "
         f"{shape['staged']['wall_ms_per_step_median']:.4f}, identical states: {same}")
     out["pages_ab_shape_65536_bf16_amsgrad"] = shape
+    return out
+
+
+def bench_decoder_7b(torch, synth, ra, dev, stream):
+    """The whole fused step over 291 tensors shaped like a 6.7B decoder
+    (BF16 grads N(0,1e-4), in-place AdamW, steady state at t = 11):
+    statistics of all gradients (13.5 GB read), hierarchical merge, 12-byte
+    read-back, clip at 1.0, update (157 launches: 226 large tensors alone,
+    the 65 norm vectors in one) -- one radamw_fused_step_multi call per step."""
+    shapes = synth.decoder_7b_shapes()
+    total = synth.total(shapes)
+    segs = []
+    for i, (_, n) in enumerate(shapes):
+        key = (0, "dec7b-bench", i)
+        p = synth.normal(n, 0.02, key + ("p",), dev)
+        g = synth.stored_grad(n, 1e-4, 1.0, "bf16", key + ("g",), dev)
+        m, v, _ = synth.steady_state(n, key, False, dev, m_std=1e-5, v_root_std=1e-4)
+        segs.append(ra.Segment(p, g, m, v, None))
+    seglist = ra.SegmentList(segs)
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=dev)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    res, step = ra.radamw_fused_step_multi(seglist, 10, opts, 1.0, 1.0, True, ws)  # warm
+    torch.cuda.synchronize()
+    times, upd = [], []
+    for k in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ra.radamw_time_next_update(a, b)
+        t0 = time.perf_counter()
+        res, step = ra.radamw_fused_step_multi(seglist, step, opts, 1.0, 1.0, True, ws)
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+        upd.append(a.elapsed_time(b))
+    ms, ums = sorted(times)[2], sorted(upd)[2]
+    out = {"tensors": len(shapes), "n_params": total, "grad_dtype": "bf16", "steps_timed": 5,
+           "step_ms_median": ms, "params_per_s": total / (ms * 1e-3), "update_ms_median": ums,
+           "update_gbs": 26 * total / (ums * 1e-3) / 1e9, "stats_and_decision_ms": ms - ums,
+           "clip_coef": res.clip_coef, "total_norm": res.total_norm, "found_inf": res.found_inf}
+    log(f"decoder 6.7B fused step: {ms:.2f} ms ({out['params_per_s']:.3g} params/s), update {ums:.2f} ms "
+        f"({out['update_gbs']:.0f} GB/s), stats + read-back {ms - ums:.2f} ms, clip {res.clip_coef:.4f}")
+    del seglist, segs, ws
+    torch.cuda.empty_cache()
     return out
 
 

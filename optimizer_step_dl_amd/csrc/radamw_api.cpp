@@ -294,10 +294,55 @@ int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, 
     return rc;
 }
 
-// Several tensors in one launch: descriptors and tile prefix sums are
-// packed into pinned host memory, copied to a device slot on the caller's
-// stream, and the slot is recycled once an event shows the kernel that read
-// it has finished.
+// Per-launch tables for the multi-tensor kernels: `fill` writes `bytes` of
+// table into pinned host memory, which is copied to a device slot on the
+// caller's stream; `launch` receives the slot's device address.  A slot is
+// recycled once an event shows that the kernel reading it has finished.
+template <typename Fill, typename Launch>
+int staged_launch(int dev, hipStream_t stream, size_t bytes, Fill fill, Launch launch) {
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.mu);
+    DeviceCache::Slot &slot = dc.slots[dc.next];
+    dc.next = (dc.next + 1) % DeviceCache::RING;
+    if (slot.pending) {
+        hipError_t e = hipEventSynchronize(slot.done);
+        if (e != hipSuccess) return hip_status(e);
+        slot.pending = false;
+    }
+    if (!slot.done) {
+        hipError_t e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    if (slot.cap < bytes) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        if (slot.dev) (void)hipFree(slot.dev);
+        slot.host = slot.dev = nullptr;
+        slot.cap = 0;
+        size_t cap = std::max<size_t>(bytes, 64 * 1024);
+        hipError_t e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_status(e);
+        e = hipMalloc(&slot.dev, cap);
+        if (e != hipSuccess) {
+            (void)hipHostFree(slot.host);
+            slot.host = nullptr;
+            return hip_status(e);
+        }
+        slot.cap = cap;
+    }
+    fill(static_cast<char *>(slot.host));
+    hipError_t e = hipMemcpyAsync(slot.dev, slot.host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = launch(static_cast<const char *>(slot.dev));
+    if (e != hipSuccess) return hip_status(e);
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    e = hipEventRecord(slot.done, stream);
+    if (e != hipSuccess) return hip_status(e);
+    slot.pending = true;
+    return RADAMW_OK;
+}
+
+// Several tensors in one launch: descriptors, tile prefix sums and the
+// coarse index go through a staged table (staged_launch).
 int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
                  int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int32_t nseg = static_cast<int32_t>(segs.size());
@@ -327,56 +372,22 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     const size_t prefix_bytes = sizeof(int64_t) * (nseg + 1);
     const size_t coarse_bytes = sizeof(int32_t) * (ncoarse + 1);
     const size_t bytes = desc_bytes + prefix_bytes + coarse_bytes;
-
     if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
-    DeviceCache &dc = g_devices[dev];
     const int grid = update_grid(tiles);
-    std::lock_guard<std::mutex> lock(dc.mu);
-    DeviceCache::Slot &slot = dc.slots[dc.next];
-    dc.next = (dc.next + 1) % DeviceCache::RING;
-    if (slot.pending) {
-        hipError_t e = hipEventSynchronize(slot.done);
-        if (e != hipSuccess) return hip_status(e);
-        slot.pending = false;
-    }
-    if (!slot.done) {
-        hipError_t e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_status(e);
-    }
-    if (slot.cap < bytes) {
-        if (slot.host) (void)hipHostFree(slot.host);
-        if (slot.dev) (void)hipFree(slot.dev);
-        slot.host = slot.dev = nullptr;
-        slot.cap = 0;
-        size_t cap = std::max<size_t>(bytes, 64 * 1024);
-        hipError_t e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
-        if (e != hipSuccess) return hip_status(e);
-        e = hipMalloc(&slot.dev, cap);
-        if (e != hipSuccess) {
-            (void)hipHostFree(slot.host);
-            slot.host = nullptr;
-            return hip_status(e);
-        }
-        slot.cap = cap;
-    }
-    char *host = static_cast<char *>(slot.host);
-    std::memcpy(host, segs.data(), desc_bytes);
-    std::memcpy(host + desc_bytes, prefix.data(), prefix_bytes);
-    std::memcpy(host + desc_bytes + prefix_bytes, coarse.data(), coarse_bytes);
-    hipError_t e = hipMemcpyAsync(slot.dev, slot.host, bytes, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_status(e);
-    const char *dev_base = static_cast<const char *>(slot.dev);
-    const SegDesc *d_segs = reinterpret_cast<const SegDesc *>(dev_base);
-    const int64_t *d_prefix = reinterpret_cast<const int64_t *>(dev_base + desc_bytes);
-    const int32_t *d_coarse = reinterpret_cast<const int32_t *>(dev_base + desc_bytes + prefix_bytes);
-    e = launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid, stream,
-                            ev_start, ev_stop);
-    if (e != hipSuccess) return hip_status(e);
-    g_launches.fetch_add(1, std::memory_order_relaxed);
-    e = hipEventRecord(slot.done, stream);
-    if (e != hipSuccess) return hip_status(e);
-    slot.pending = true;
-    return RADAMW_OK;
+    return staged_launch(
+        dev, stream, bytes,
+        [&](char *host) {
+            std::memcpy(host, segs.data(), desc_bytes);
+            std::memcpy(host + desc_bytes, prefix.data(), prefix_bytes);
+            std::memcpy(host + desc_bytes + prefix_bytes, coarse.data(), coarse_bytes);
+        },
+        [&](const char *dev_base) {
+            const SegDesc *d_segs = reinterpret_cast<const SegDesc *>(dev_base);
+            const int64_t *d_prefix = reinterpret_cast<const int64_t *>(dev_base + desc_bytes);
+            const int32_t *d_coarse = reinterpret_cast<const int32_t *>(dev_base + desc_bytes + prefix_bytes);
+            return launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid,
+                                       stream, ev_start, ev_stop);
+        });
 }
 
 // Validated multi-tensor update (shared by radamw_step_multi, the write-back
@@ -901,17 +912,32 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
         if ((rc = check_alias(ranges))) return rc;
     }
 
-    // statistics of every active gradient, rows packed back to back
+    // statistics of every active gradient, rows packed back to back in one
+    // launch (the same records per-tensor launches would write)
     StatsRec *rows = static_cast<StatsRec *>(workspace);
     int64_t nrows = 0;
+    std::vector<StatsSeg> st;
+    st.reserve(static_cast<size_t>(active));
     for (int32_t i = 0; i < nseg; ++i) {
         const radamw_segment &s = segs[i];
         if (s.n == 0) continue;
         const int64_t r = stats_rows(s.n, gdt);
-        rc = hip_status(launch_analyze(s.grad, gdt, s.n, stats_head(s.grad, gdt, s.n), r, rows + nrows, stream));
+        st.push_back(StatsSeg{s.grad, s.n, nrows, stats_head(s.grad, gdt, s.n), static_cast<int32_t>(r)});
+        nrows += r;
+    }
+    if (st.size() == 1) {
+        rc = hip_status(launch_analyze(st[0].g, gdt, st[0].n, st[0].head, st[0].rows, rows, stream));
         if (rc) return rc;
         g_launches.fetch_add(1, std::memory_order_relaxed);
-        nrows += r;
+    } else {
+        const size_t bytes = sizeof(StatsSeg) * st.size();
+        rc = staged_launch(
+            dev, stream, bytes, [&](char *host) { std::memcpy(host, st.data(), bytes); },
+            [&](const char *dev_base) {
+                return launch_analyze_table(reinterpret_cast<const StatsSeg *>(dev_base),
+                                            static_cast<int32_t>(st.size()), nrows, gdt, rows, stream);
+            });
+        if (rc) return rc;
     }
     int64_t se;
     int32_t ex;

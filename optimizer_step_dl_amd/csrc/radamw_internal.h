@@ -126,12 +126,25 @@ hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_pref
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
                                const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
                                hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+// One gradient of a multi-tensor statistics launch: its records are
+// out[row_begin, row_begin + rows), laid out exactly as a single-tensor
+// launch would write them.
+struct StatsSeg {
+    const void *g;
+    int64_t n;
+    int64_t row_begin;
+    int32_t head;
+    int32_t rows;
+};
+
 // The staged (unfused) baseline: 4 launches (5 with vmax != null); *launched
 // receives how many were submitted.
 hipError_t launch_staged(float *p, const void *g, int gdt, float *m, float *v, float *vmax, float *delta,
                          int64_t n, bool first, const Coefs &c, hipStream_t stream, int *launched);
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream);
+hipError_t launch_analyze_table(const StatsSeg *segs_dev, int32_t nseg, int64_t total_rows, int gdt,
+                                StatsRec *out, hipStream_t stream);
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
                         StatsRec *out, hipStream_t stream);
 

@@ -108,12 +108,13 @@ __device__ __forceinline__ void block_finish(double s, uint64_t count, StatsRec 
     }
 }
 
-// Elements [0, head) and the tail after the last whole 16-byte chunk are
-// scalar (workgroup 0); the body is walked in passes of STATS_BLOCK *
-// STATS_UNROLL chunks, workgroup b taking passes b, b + rows, b + 2 rows ...
+// Row r of one gradient's analysis: elements [0, head) and the tail after
+// the last whole 16-byte chunk are scalar (row 0); the body is walked in
+// passes of STATS_BLOCK * STATS_UNROLL chunks, row r taking passes r,
+// r + rows, r + 2 rows ...
 template <int GDT>
-__global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64_t n, int32_t head,
-                                                            int64_t rows, StatsRec *out) {
+__device__ __forceinline__ void analyze_row(const void *g, int64_t n, int32_t head, int64_t rows, int64_t r,
+                                            StatsRec *out) {
     constexpr int EPC = GDT == G_F32 ? 4 : 8;  // elements per 16-byte chunk
     constexpr int64_t PASS = int64_t(STATS_BLOCK) * STATS_UNROLL;
     const int tid = threadIdx.x;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64
     Acc a;
     a.s[0] = a.s[1] = a.s[2] = a.s[3] = 0.0;
     a.bad = 0;
-    for (int64_t base = int64_t(blockIdx.x) * PASS; base < body; base += rows * PASS) {
+    for (int64_t base = r * PASS; base < body; base += rows * PASS) {
         if (base + PASS <= body) {
 #pragma unroll
             for (int u = 0; u < STATS_UNROLL; ++u) acc_chunk<GDT>(a, gb, base + u * STATS_BLOCK + tid);
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64
             }
         }
     }
-    if (blockIdx.x == 0) {
+    if (r == 0) {
         const int64_t tail = n - head - body * EPC;
         if (tid < head + tail) {
             const int64_t e = tid < head ? int64_t(tid) : head + body * EPC + (tid - head);
@@ -143,7 +144,30 @@ __global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64
         }
     }
     const double s = (a.s[0] + a.s[1]) + (a.s[2] + a.s[3]);
-    block_finish<STATS_BLOCK>(s, a.bad, out + blockIdx.x);
+    block_finish<STATS_BLOCK>(s, a.bad, out);
+}
+
+// One gradient: workgroup b writes record b.
+template <int GDT>
+__global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64_t n, int32_t head,
+                                                            int64_t rows, StatsRec *out) {
+    analyze_row<GDT>(g, n, head, rows, blockIdx.x, out + blockIdx.x);
+}
+
+// Several gradients in one launch: workgroup b finds the gradient whose
+// records include b (binary search over row_begin) and computes the same
+// record a single-tensor launch would, so the reports are bit-identical.
+template <int GDT>
+__global__ __launch_bounds__(STATS_BLOCK) void grad_analyze_table(const StatsSeg *__restrict__ segs,
+                                                                  int32_t nseg, StatsRec *out) {
+    const int64_t b = blockIdx.x;
+    int32_t lo = 0, hi = nseg;  // segs[lo].row_begin <= b < segs[hi].row_begin (hi == nseg: end)
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (segs[mid].row_begin <= b) lo = mid; else hi = mid;
+    }
+    const StatsSeg sg = segs[lo];
+    analyze_row<GDT>(sg.g, sg.n, sg.head, sg.rows, b - sg.row_begin, out + b);
 }
 
 // Workgroup b reduces records [b * per_block, min(nin, (b + 1) * per_block)).
@@ -176,6 +200,18 @@ hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64
         break;
     default:
         return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_analyze_table(const StatsSeg *segs_dev, int32_t nseg, int64_t total_rows, int gdt,
+                                StatsRec *out, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(total_rows)), block(STATS_BLOCK);
+    switch (gdt) {
+    case G_F32: hipLaunchKernelGGL(grad_analyze_table<G_F32>, grid, block, 0, stream, segs_dev, nseg, out); break;
+    case G_F16: hipLaunchKernelGGL(grad_analyze_table<G_F16>, grid, block, 0, stream, segs_dev, nseg, out); break;
+    case G_BF16: hipLaunchKernelGGL(grad_analyze_table<G_BF16>, grid, block, 0, stream, segs_dev, nseg, out); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -161,7 +161,9 @@ def _fused_case(sizes, gdt, inject, max_norm, key, step0=0, amsgrad=False, hiera
     if skip_ref:
         assert not res.updated and step == step0
         assert all(torch.equal(a, s.param) for a, s in zip(snap, segs))
-        assert launched == nstats + 1 + ra.radamw_stats_plan(sum(ra.radamw_grad_stats_rows(n, TORCH_GDT[gdt]) for n in sizes))[1]
+        # one analysis launch for the whole list, the merge levels, the final merge; no update
+        extra = ra.radamw_stats_plan(sum(ra.radamw_grad_stats_rows(n, TORCH_GDT[gdt]) for n in sizes))[1]
+        assert nstats > 1 and launched == 1 + extra + 1
     else:
         assert res.updated and step == step0 + 1
         for (p_ref, st_ref), s in zip(refs, segs):
@@ -187,3 +189,28 @@ def test_fused_step_found_inf_skips_everything():
     announce("fused found_inf")
     res = _fused_case([4096, 1_000_000, 2049], "bf16", 3, 1.0, (0, "fi"), step0=4)
     assert res.found_inf and res.nonfinite == 3
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_fused_statistics_launch_equals_per_tensor_launches(gdt):
+    """radamw_fused_step_multi analyses all gradients in one launch; its
+    report is bit-identical to per-tensor radamw_grad_stats launches
+    followed by the same merge (same rows, same order)."""
+    announce(f"fused stats table {gdt}")
+    sizes = [4096, 3, 9_000_001, 2047, 1_000_000, 8193, 65536]
+    grads = [synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "fst", gdt, i)).to(DEV) for i, n in enumerate(sizes)]
+    _inject(grads[2], 4, (0, "fst", gdt, "pos"))
+    s_ref, c_ref, rows = _stats_gpu(grads, True)
+    assert rows > 1024
+    segs = []
+    for i, g in enumerate(grads):
+        n = g.numel()
+        segs.append(ra.Segment(torch.zeros(n, device=DEV), g, torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)))
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(segs), dtype=torch.uint8, device=DEV)
+    before = ra.radamw_launch_count()
+    res, step = ra.radamw_fused_step_multi(segs, 3, ra.options(), 1.0, 1.0, True, ws)
+    torch.cuda.synchronize()
+    assert res.found_inf and not res.updated and step == 3
+    assert res.nonfinite == c_ref == 4 and res.sumsq == s_ref
+    extra = ra.radamw_stats_plan(rows)[1]
+    assert ra.radamw_launch_count() - before == 1 + extra + 1  # one analysis launch, merges, final merge

@@ -45,8 +45,14 @@ constexpr int64_t UPDATE_MAX_GRID = 0x7fffffff;
 // Statistics: 256-lane analysis workgroups, each lane loads STATS_UNROLL
 // 16-byte chunks per pass; one record ("row") per workgroup.
 constexpr int STATS_BLOCK = 256;
-constexpr int STATS_UNROLL = 4;
-constexpr int64_t STATS_ROWS_CAP = 2048;     // records per analysis launch, at most
+#ifndef RADAMW_STATS_UNROLL
+#define RADAMW_STATS_UNROLL 4
+#endif
+constexpr int STATS_UNROLL = RADAMW_STATS_UNROLL;
+#ifndef RADAMW_STATS_ROWS_CAP
+#define RADAMW_STATS_ROWS_CAP 8192
+#endif
+constexpr int64_t STATS_ROWS_CAP = RADAMW_STATS_ROWS_CAP;  // records per tensor, at most
 constexpr int MERGE_BLOCK = 1024;            // merge workgroup = fan-in
 constexpr int64_t MERGE_FAN_IN = 1024;
 constexpr int64_t STATS_MAX_ROWS = 4194304;  // accepted by the merge plan

@@ -36,23 +36,59 @@ __device__ __forceinline__ void acc_value(Acc &a, int slot, float x) {
     a.bad += finite ? 0u : 1u;
 }
 
+// A finite value: add its exact square (binary64) to slot `slot`.
+__device__ __forceinline__ void acc_finite(Acc &a, int slot, float x) {
+    const double d = static_cast<double>(x);
+    a.s[slot] = __builtin_fma(d, d, a.s[slot]);
+}
+
+// For a 32-bit word holding two 16-bit values whose exponent field is `exp`
+// (0x7f80 bfloat16, 0x7c00 binary16): bit 15 / bit 31 of the result is set
+// exactly when the low / high value has an all-ones exponent (inf or NaN),
+// since adding the field's lowest bit carries into the value's sign position
+// only from all ones.
+template <uint32_t EXP>
+__device__ __forceinline__ uint32_t nonfinite_pairs(uint32_t w) {
+    constexpr uint32_t field = EXP | (EXP << 16);
+    constexpr uint32_t low_bit = (EXP & (~EXP + 1u)) | ((EXP & (~EXP + 1u)) << 16);
+    return ((w & field) + low_bit) & 0x80008000u;
+}
+
 template <int GDT>
 __device__ __forceinline__ void acc_chunk(Acc &a, const void *g, int64_t chunk) {
     if constexpr (GDT == G_F32) {
         const f32x4 x = __builtin_nontemporal_load(gl(reinterpret_cast<const f32x4 *>(g)) + chunk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc_value(a, j, x[j]);
-    } else if constexpr (GDT == G_F16) {
-        const f16x8 h = __builtin_nontemporal_load(gl(reinterpret_cast<const f16x8 *>(g)) + chunk);
-        const f32x8 x = __builtin_convertvector(h, f32x8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc_value(a, j & 3, x[j]);
     } else {
+        // 16-bit values: one integer test per word flags non-finite pairs;
+        // clean words (the usual case) skip the per-value selects
         const u32x4 w = __builtin_nontemporal_load(gl(reinterpret_cast<const u32x4 *>(g)) + chunk);
+        constexpr uint32_t EXP = GDT == G_F16 ? 0x7c00u : 0x7f80u;
+        const uint32_t bad = nonfinite_pairs<EXP>(w[0]) | nonfinite_pairs<EXP>(w[1]) |
+                             nonfinite_pairs<EXP>(w[2]) | nonfinite_pairs<EXP>(w[3]);
+        if (bad == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc_value(a, j, __builtin_bit_cast(float, w[j] << 16));
-            acc_value(a, j, __builtin_bit_cast(float, w[j] & 0xffff0000u));
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (GDT == G_F16) {
+                    acc_finite(a, j, static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j]))));
+                    acc_finite(a, j, static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16))));
+                } else {
+                    acc_finite(a, j, __builtin_bit_cast(float, w[j] << 16));
+                    acc_finite(a, j, __builtin_bit_cast(float, w[j] & 0xffff0000u));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (GDT == G_F16) {
+                    acc_value(a, j, static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j]))));
+                    acc_value(a, j, static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16))));
+                } else {
+                    acc_value(a, j, __builtin_bit_cast(float, w[j] << 16));
+                    acc_value(a, j, __builtin_bit_cast(float, w[j] & 0xffff0000u));
+                }
+            }
         }
     }
 }

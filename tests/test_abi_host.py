@@ -78,7 +78,7 @@ def test_grad_stats_rows_is_deterministic_and_bounded(lib):
         prev = 0
         for n in (1, 100, 4096, 8192, 8193, 10**6, 10**8, 5 * 10**9):
             r = ra.radamw_grad_stats_rows(n, dt)
-            assert 1 <= r <= 2048 and r >= prev
+            assert 1 <= r <= 8192 and r >= prev
             prev = r
     # the 6.7B-parameter list stays far inside the plan's row limit
     import synth

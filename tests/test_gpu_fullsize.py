@@ -218,3 +218,50 @@ def test_decoder_7b_list_stats_clip_skip_sequence():
         s.grad.copy_(synth.stored_grad(s.grad.numel(), 1e-4, 1.0, "bf16", (0, "dec7b", i, "g3"), DEV))
     res, step = fused(step, 3)
     assert step == 2 and res.updated and not res.found_inf
+
+
+def test_single_tensor_beyond_32_bit_indexing():
+    """One tensor of 2^32 + 1029 elements (64-bit indexing in every kernel):
+    in-place AdamW with BF16 grads at t = 3 and its statistics.  Oracle on
+    sampled elements around 2^31, 2^32 and the ragged end; statistics over
+    every element (count exact, sum within the sequential bound)."""
+    n = (1 << 32) + 1029
+    announce(f"single tensor n={n}")
+    p = synth.normal(n, 0.02, (0, "huge", "p"), DEV)
+    g = synth.stored_grad(n, 1e-3, 1.0, "bf16", (0, "huge", "g"), DEV)
+    m, v, _ = synth.steady_state(n, (0, "huge"), False, DEV)
+    g[(1 << 32) + 17] = float("inf")
+    g[(1 << 31) - 1] = float("nan")
+    opts = ra.options(lr=1e-3, weight_decay=0.01)
+    rng = np.random.Generator(np.random.PCG64(11))
+    idx = np.unique(np.concatenate([np.arange(0, 512), np.arange((1 << 31) - 512, (1 << 31) + 512),
+                                    np.arange((1 << 32) - 512, n), rng.integers(0, n, 20000)]))
+    idx_dev = torch.from_numpy(idx).to(DEV)
+    before = [_gather(t, idx_dev) for t in (p, g, m, v, None)]
+    # statistics over everything
+    rows = ra.radamw_grad_stats_rows(n, torch.bfloat16)
+    rows_buf = torch.zeros(3 * rows, dtype=torch.int32, device=DEV)
+    assert ra.radamw_grad_stats(g, rows_buf) == rows
+    se, _ = ra.radamw_stats_plan(rows)
+    report = torch.zeros(3, dtype=torch.int32, device=DEV)
+    ra.radamw_merge_stats(rows_buf, rows, torch.zeros(max(se, 1), device=DEV) if se else None, report, True)
+    rep = ra.radamw_read_report(report)
+    acc = oracle.StatsAccumulator()
+    chunk = 1 << 28
+    for lo in range(0, n, chunk):
+        acc.add(grad_host(g[lo:lo + chunk]), "bf16")
+    s_ref, c_ref = acc.result
+    assert rep.nonfinite == c_ref == 2
+    assert abs(rep.sumsq - s_ref) <= (n - 1) * 2.0**-53 * s_ref
+    # the update (non-finite elements are outside the formula's contract: masked below)
+    updated, step = ra.radamw_step_multi([ra.Segment(p, g, m, v)], 2, opts, ra.control(1.0))
+    assert updated and step == 3
+    torch.cuda.synchronize()
+    p_ref, st_ref = _oracle_on_sample(*before, 2, opts, 1.0, "bf16")
+    x = torch.from_numpy(synth.grad_numpy(before[1]).view(np.int16)).view(torch.bfloat16).float().numpy()
+    ok = np.isfinite(x)
+    after_p = _gather(p, idx_dev).numpy()
+    after_v = _gather(v, idx_dev).numpy()
+    contract_one_step(after_p[ok], p_ref[ok], "p")
+    contract_one_step(after_v[ok], st_ref.exp_avg_sq[ok], "v")
+    assert ok.sum() == ok.size - 2

@@ -4,20 +4,22 @@
                     [--no-cpu-baseline] [--copy-calibration]
 
 One timed step is one pass of the whole path over a 268,435,456-element flat
-FP32 bucket (FP32 gradients, steady state at t = 1000, moments pre-warmed):
-gradient statistics (radamw_grad_stats), the hierarchical fan-in-1024 merge
-(radamw_merge_stats), the 12-byte report read back to the host
-(radamw_read_report, the step's one synchronisation), the skip / clip
-decision (radamw_decide, global norm clipped at 1.0), and the in-place fused
-update (radamw_step_multi over the bucket).  Inputs are resident in HBM
-before the timer starts.  HIP events recorded on the launch stream around
-every update and statistics launch inside the timed region give the
-per-kernel durations the roofline object uses.
+FP32 bucket (FP32 gradients, steady state at t = 1000, moments pre-warmed),
+one radamw_fused_step_multi call: gradient statistics, the hierarchical
+fan-in-1024 merge, the 12-byte report read back to the host (the step's one
+synchronisation), the skip / clip decision (global norm clipped at 1.0), and
+the in-place fused update.  Inputs are resident in HBM before the timer
+starts.  Inside the timed region the update kernel's own start / end HIP
+events (radamw_time_next_update: hipExtLaunchKernelGGL on the launch stream)
+give the kernel duration the roofline object uses.
 
 Prints ONE JSON line (rank 0).  Extra keys beside the contract's:
-"roofline", "cpu_baseline", "kernels" (per-kernel event timings),
-"variants" (update-only timings of the other configurations of the bucket),
-"copy_ceiling" (torch device-to-device copy bandwidth, context only).
+"roofline", "cpu_baseline", "kernels" (update kernel timing, rest of the
+step), "variants" (update-only timings of the bucket's other
+configurations), "staged_vs_fused" (the pages' staged baseline A/B),
+"decoder_1b_list" (per-tensor vs radamw_step_multi launches),
+"decoder_7b_fused_step" (the whole step over a 6.7B-parameter list),
+"copy_ceiling" (torch elementwise copy bandwidth, context only).
 """
 from __future__ import annotations
 
@@ -123,75 +125,60 @@ def main(argv=None):
     # ---------------------------------------------------- headline step --
     p, g, m, v, _ = build_inputs(torch, synth, n, "adamw", "f32", dev)
     opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    seglist = ra.SegmentList([ra.Segment(p, g, m, v, None)])
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     step = ctypes.c_uint64(999)
-    seg = (_abi._Segment * 1)(_abi._Segment(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), None, n))
+    result = _abi.FusedResult()
+    max_norm = 1.0
     rows_n = lib.radamw_grad_stats_rows(n, 0)
     se, ex = ra.radamw_stats_plan(rows_n)
-    rows = torch.zeros(3 * rows_n, dtype=torch.int32, device=dev)
-    scratch = torch.zeros(max(se, 1), dtype=torch.float32, device=dev)
-    report = torch.zeros(3, dtype=torch.int32, device=dev)
-    host_report = _abi.Stats()
-    written = ctypes.c_int64()
-    ctrl = _abi.Control()
-    result = _abi.FusedResult()
-    updated = ctypes.c_int32()
-    max_norm = 1.0
-    check = lambda rc, w: rc == 0 or (_ for _ in ()).throw(ra.RadamwError(rc, w))
 
     def one_step(ev=None):
+        # the whole step in one C call: statistics -> merge -> read-back ->
+        # decision -> update; ev: the update kernel's own start/end events
+        # (the launch follows the read-back synchronisation, so events
+        # recorded from the host around it would also time the submission)
         if ev is not None:
-            ev[0].record(stream)
-            # the update kernel's own start/end (hipExtLaunchKernelGGL events):
-            # the launch follows the read-back synchronisation, so events
-            # recorded from the host around it would also time the submission
-            lib.radamw_time_next_update(ev[2].cuda_event, ev[3].cuda_event)
-        check(lib.radamw_grad_stats(g.data_ptr(), 0, n, rows.data_ptr(), rows_n, ctypes.byref(written), sptr),
-              "grad_stats")
-        check(lib.radamw_merge_stats(rows.data_ptr(), rows_n, scratch.data_ptr(), se, report.data_ptr(), 1, sptr),
-              "merge_stats")
-        if ev is not None:
-            ev[1].record(stream)
-        check(lib.radamw_read_report(report.data_ptr(), ctypes.byref(host_report), sptr), "read_report")
-        check(lib.radamw_decide(ctypes.byref(host_report), 1.0, max_norm, ctypes.byref(ctrl),
-                                ctypes.byref(result)), "decide")
-        if ctrl.skip_update:
+            lib.radamw_time_next_update(ev[0].cuda_event, ev[1].cuda_event)
+        rc = lib.radamw_fused_step_multi(seglist.array, 1, seglist.code, ctypes.byref(step), ctypes.byref(opts),
+                                         1.0, max_norm, 1, ws_ptr, ws_bytes, sptr, ctypes.byref(result))
+        if rc != 0:
+            raise ra.RadamwError(rc, "radamw_fused_step_multi")
+        if not result.updated:
             raise RuntimeError("unexpected non-finite gradient in the benchmark bucket")
-        check(lib.radamw_step_multi(seg, 1, 0, ctypes.byref(step), ctypes.byref(opts), ctypes.byref(ctrl), sptr,
-                                    ctypes.byref(updated)), "step_multi")
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for ev in events:  # create the device events before handing them to the library
         for e in ev:
             e.record(stream)
-    log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for k in range(args.steps):
         one_step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    upd_ms = [e[2].elapsed_time(e[3]) for e in events]
-    stats_ms = [e[0].elapsed_time(e[1]) for e in events]
+    upd_ms = [e[0].elapsed_time(e[1]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
     value = n / (ms_per_step * 1e-3)
     upd_avg = sum(upd_ms) / len(upd_ms)
-    stats_avg = sum(stats_ms) / len(stats_ms)
     bpp = BYTES_PER_PARAM[("adamw", "f32", False)]
     achieved = bpp * n / (upd_avg * 1e-3) / 1e9
     traffic = counters_from_profile()
-    log(f"step {ms_per_step:.3f} ms, update {upd_avg:.3f} ms ({achieved:.0f} GB/s), stats+merge {stats_avg:.3f} ms, "
-        f"clip {result.clip_coef:.4f}, norm {result.total_norm:.4f}")
+    log(f"step {ms_per_step:.3f} ms, update {upd_avg:.3f} ms ({achieved:.0f} GB/s), statistics + merge + "
+        f"read-back + decision {ms_per_step - upd_avg:.3f} ms, clip {result.clip_coef:.4f}, norm {result.total_norm:.4f}")
     kernels = {
         "update_adamw_f32_inplace": {"avg_ms": upd_avg, "min_ms": min(upd_ms), "max_ms": max(upd_ms),
                                      "bytes_per_param": bpp, "gbs": achieved},
-        "grad_stats_plus_merge": {"avg_ms": stats_avg, "min_ms": min(stats_ms), "max_ms": max(stats_ms),
-                                  "bytes_per_param": 4, "gbs": 4 * n / (stats_avg * 1e-3) / 1e9,
-                                  "rows": rows_n, "extra_merge_kernels": ex},
+        "rest_of_step": {"avg_ms": ms_per_step - upd_avg, "what": "grad statistics (4 B/param read), "
+                         f"{ex} merge level(s) + final merge, 12-byte read-back, decision, launch latencies",
+                         "rows": rows_n, "extra_merge_kernels": ex},
     }
-    del p, g, m, v, rows, scratch
+    del p, g, m, v, ws, seglist
     torch.cuda.empty_cache()
 
     # ------------------------------------------------ update-only variants --

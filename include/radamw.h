@@ -317,7 +317,10 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale,
  * (hierarchical) merge -> 12-byte report read back -> skip or clip decision
  * -> one in-place radamw_step_multi launch.
  *   workspace : device, >= radamw_fused_workspace_bytes(...) bytes, 4-byte
- *               aligned, caller-owned (rows, merge scratch and report).
+ *               aligned, caller-owned (rows, merge scratch and a reserved
+ *               report slot).  The final merge writes the report directly
+ *               into host memory the library maps for the device, so the
+ *               read-back is the stream synchronisation alone.
  *   max_grad_norm <= 0 disables clipping.
  *   result    : host struct, always filled on RADAMW_OK.
  * Synchronises the stream once (the report read-back).

@@ -56,6 +56,11 @@ struct DeviceCache {
     int next = 0;
     // pinned 12-byte staging for report read-back
     radamw_stats *pinned_report = nullptr;
+    // host memory mapped for the device: the fused step's final merge writes
+    // its report here directly, so the read-back is only the synchronisation
+    std::mutex report_mu;
+    radamw_stats *mapped_report_host = nullptr;
+    radamw_stats *mapped_report_dev = nullptr;
 };
 
 DeviceCache g_devices[MAX_DEVICES];
@@ -943,11 +948,33 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     int32_t ex;
     plan(nrows, &se, &ex);
     StatsRec *scratch = rows + nrows;
-    StatsRec *report = scratch + se / 3;
-    if ((rc = merge_launch(rows, nrows, scratch, report, hierarchical != 0, stream))) return rc;
+    StatsRec *report = scratch + se / 3;  // reserved in the workspace layout
 
+    (void)report;
     radamw_stats host;
-    if ((rc = read_report(report, &host, dev, stream))) return rc;
+    {
+        // the final merge writes straight into mapped host memory; the
+        // stream synchronisation is the read-back
+        DeviceCache &dc = g_devices[dev];
+        std::lock_guard<std::mutex> lock(dc.report_mu);
+        if (!dc.mapped_report_host) {
+            void *hp = nullptr, *dp = nullptr;
+            hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
+            if (e != hipSuccess) return hip_status(e);
+            e = hipHostGetDevicePointer(&dp, hp, 0);
+            if (e != hipSuccess) {
+                (void)hipHostFree(hp);
+                return hip_status(e);
+            }
+            dc.mapped_report_host = static_cast<radamw_stats *>(hp);
+            dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
+        }
+        StatsRec *mapped = reinterpret_cast<StatsRec *>(dc.mapped_report_dev);
+        if ((rc = merge_launch(rows, nrows, scratch, mapped, hierarchical != 0, stream))) return rc;
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_status(e);
+        std::memcpy(&host, dc.mapped_report_host, sizeof host);
+    }
     radamw_control ctrl;
     radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
     if (ctrl.skip_update) {

@@ -279,9 +279,10 @@ def main(argv=None):
         del a, b
 
     # --------------------------------------------------- CPU oracle --
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, synth, args.cpu_seconds)
+        cpu_all = cpu_baseline_threads(torch, synth, max(1.0, args.cpu_seconds / 4))
 
     out = {
         "metric": METRIC,
@@ -308,6 +309,7 @@ def main(argv=None):
                      "kernel": "adamw_update_single<f32, adamw, steady>",
                      "algorithmic_bytes_per_launch": bpp * n},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "kernels": kernels,
         "variants": variants,
         "copy_ceiling": copy_ceiling,
@@ -315,7 +317,8 @@ def main(argv=None):
         "staged_vs_fused": staged,
         "decoder_7b_fused_step": decoder7,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
-                   "torch": torch.__version__, "hip": torch.version.hip},
+                   "torch": torch.__version__, "hip": torch.version.hip,
+                   "memory_bytes": props.total_memory, "clocks": clocks()},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -413,8 +416,10 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
     """The whole fused step over 291 tensors shaped like a 6.7B decoder
     (BF16 grads N(0,1e-4), in-place AdamW, steady state at t = 11):
     statistics of all gradients (13.5 GB read), hierarchical merge, 12-byte
-    read-back, clip at 1.0, update (157 launches: 226 large tensors alone,
-    the 65 norm vectors in one) -- one radamw_fused_step_multi call per step."""
+    read-back, clip at 1.0, update (227 launches: 226 large tensors alone,
+    the 65 norm vectors in one).  Timed twice: one radamw_fused_step_multi
+    call per step (every call validates 1164 buffers), then the same steps
+    through a persistent tensor list (validated once)."""
     shapes = synth.decoder_7b_shapes()
     total = synth.total(shapes)
     segs = []
@@ -427,27 +432,42 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
     seglist = ra.SegmentList(segs)
     ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=dev)
     opts = ra.options(lr=1e-3, weight_decay=1e-4)
-    res, step = ra.radamw_fused_step_multi(seglist, 10, opts, 1.0, 1.0, True, ws)  # warm
+
+    def timed(call, step):
+        times, upd = [], []
+        for k in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ra.radamw_time_next_update(a, b)
+            t0 = time.perf_counter()
+            res, step = call(step)
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+            upd.append(a.elapsed_time(b))
+        return sorted(times)[2], sorted(upd)[2], res, step
+
+    per_call = lambda st: ra.radamw_fused_step_multi(seglist, st, opts, 1.0, 1.0, True, ws)
+    res, step = per_call(10)  # warm
     torch.cuda.synchronize()
-    times, upd = [], []
-    for k in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ra.radamw_time_next_update(a, b)
-        t0 = time.perf_counter()
-        res, step = ra.radamw_fused_step_multi(seglist, step, opts, 1.0, 1.0, True, ws)
-        torch.cuda.synchronize()
-        times.append((time.perf_counter() - t0) * 1e3)
-        upd.append(a.elapsed_time(b))
-    ms, ums = sorted(times)[2], sorted(upd)[2]
+    ms_call, ums_call, res, step = timed(per_call, step)
+    lst = ra.TensorList(seglist, False)
+    listed = lambda st: lst.fused_step(st, opts, 1.0, 1.0, True)
+    res, step = listed(step)  # warm
+    torch.cuda.synchronize()
+    ms, ums, res, step = timed(listed, step)
+    lst.close()
     out = {"tensors": len(shapes), "n_params": total, "grad_dtype": "bf16", "steps_timed": 5,
+           "path": "radamw_list_fused_step (persistent tensor list)",
            "step_ms_median": ms, "params_per_s": total / (ms * 1e-3), "update_ms_median": ums,
            "update_gbs": 26 * total / (ums * 1e-3) / 1e9, "stats_and_decision_ms": ms - ums,
+           "per_call": {"path": "radamw_fused_step_multi (validates every call)", "step_ms_median": ms_call,
+                        "update_ms_median": ums_call, "stats_and_decision_ms": ms_call - ums_call},
            "clip_coef": res.clip_coef, "total_norm": res.total_norm, "found_inf": res.found_inf}
-    log(f"decoder 6.7B fused step: {ms:.2f} ms ({out['params_per_s']:.3g} params/s), update {ums:.2f} ms "
-        f"({out['update_gbs']:.0f} GB/s), stats + read-back {ms - ums:.2f} ms, clip {res.clip_coef:.4f}")
+    log(f"decoder 6.7B fused step (list): {ms:.2f} ms ({out['params_per_s']:.3g} params/s), update {ums:.2f} ms "
+        f"({out['update_gbs']:.0f} GB/s), stats + read-back {ms - ums:.2f} ms; per call {ms_call:.2f} ms; "
+        f"clip {res.clip_coef:.4f}")
     del seglist, segs, ws
     torch.cuda.empty_cache()
     return out
@@ -501,19 +521,24 @@ def bench_decoder_list(torch, synth, ra, dev, stream):
     return out
 
 
-def cpu_baseline(torch, synth, seconds):
-    """The oracle's full step (statistics, decision, update) on a bounded
-    sample of the same bucket: the first 2^24 elements, drawn on the CPU with
-    the same recipe; repeated until `seconds` have passed.  One core."""
-    import numpy as np
+def _cpu_sample(synth, n):
     import oracle
-    n = 1 << 24
     key = (0, "bucket-cpu", n)
     p = synth.normal(n, 0.02, key + ("p",)).numpy().copy()
     g = synth.grad_numpy(synth.stored_grad(n, 1e-3, 1.0, "f32", key + ("g",)))
     m, v, _ = synth.steady_state(n, key, False)
     st = oracle.State.__new__(oracle.State)
     st.step, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq = 999, m.numpy().copy(), v.numpy().copy(), None
+    return p, g, st
+
+
+def cpu_baseline(torch, synth, seconds):
+    """The oracle's full step (statistics, decision, update) on a bounded
+    sample of the same bucket: the first 2^24 elements, drawn on the CPU with
+    the same recipe; repeated until `seconds` have passed.  One core."""
+    import oracle
+    n = 1 << 24
+    p, g, st = _cpu_sample(synth, n)
     opts = oracle.Options(lr=1e-3, weight_decay=1e-4)
     steps = 0
     t0 = time.perf_counter()
@@ -530,6 +555,56 @@ def cpu_baseline(torch, synth, seconds):
             "sample": f"first 2^24 = {n:,} elements of the same bucket recipe (CPU draws), full step "
                       f"(stats + decision + update), {steps} steps in {el:.1f} s, single thread",
             "bytes_per_param_model": 28}
+
+
+def cpu_baseline_threads(torch, synth, seconds):
+    """The same oracle step on all host cores this process may use (at most
+    16): the element range is split into one contiguous slice per thread and
+    every thread runs the oracle's own scalar loops on its slice (ctypes
+    releases the GIL).  The update is elementwise, so the slices compute
+    exactly what one call would; the per-slice sums of squares are added
+    afterwards, which changes only their FP64 rounding order."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    n = 1 << 24
+    p, g, st = _cpu_sample(synth, n)
+    opts = oracle.Options(lr=1e-3, weight_decay=1e-4)
+    bounds = [(n * k // cores, n * (k + 1) // cores) for k in range(cores)]
+    states = []
+    for lo, hi in bounds:
+        s = oracle.State.__new__(oracle.State)
+        s.step, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq = st.step, st.exp_avg[lo:hi], st.exp_avg_sq[lo:hi], None
+        states.append(s)
+    steps = 0
+    with ThreadPoolExecutor(max_workers=cores) as pool:
+        t0 = time.perf_counter()
+        while True:
+            parts = list(pool.map(lambda b: oracle.grad_stats(g[b[0]:b[1]], "f32"), bounds))
+            skip, eff = oracle.decide(sum(s for s, _ in parts), sum(c for _, c in parts), 1.0, 1.0)
+            list(pool.map(lambda k: oracle.adamw_step(p[bounds[k][0]:bounds[k][1]], g[bounds[k][0]:bounds[k][1]],
+                                                      "f32", states[k], opts, eff, skip), range(cores)))
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    log(f"cpu oracle on {cores} threads: {steps} steps of {n} elements in {el:.1f} s")
+    return {"value": n * steps / el, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"first 2^24 = {n:,} elements of the same bucket recipe, full step, element range split "
+                      f"into {cores} contiguous slices (one thread each), {steps} steps in {el:.1f} s"}
+
+
+def clocks():
+    """GPU clock levels as rocm-smi reports them (best effort; None if the
+    tool is missing or says nothing)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+        card = next(iter(data.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk"))}
+    except Exception:
+        return None
 
 
 if __name__ == "__main__":

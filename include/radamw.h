@@ -26,7 +26,9 @@
  *     call; a multi-kernel entry point may have submitted earlier kernels,
  *     and the caller should treat the device state as unconfirmed (FA-ja
  *     "低レベルの使用": discard unconfirmed outputs after a device fault).
- *     The library keeps no pointer after a call returns.
+ *     The library keeps no pointer after a call returns, except a
+ *     persistent tensor list (radamw_list_create), which keeps its
+ *     segments' pointers until radamw_list_destroy.
  *   - There is no device-side step counter: the completed-step count lives
  *     in host memory owned by the caller, and the bias-correction
  *     coefficients are computed on the host for every call, so a captured
@@ -335,6 +337,74 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
                             radamw_stream_t stream, radamw_fused_result *result);
 
 /*
+ * Persistent tensor lists.  A training run updates the same tensors step
+ * after step, and validating a list of a few hundred separately allocated
+ * tensors (two HIP pointer queries per allocation, the overlap sweep)
+ * costs about 0.6 ms of host time per call before the first kernel can
+ * start.  radamw_list_create validates a segment list once and computes
+ * everything that depends only on the tensors: the launch split of
+ * radamw_step_multi, the update descriptors, the statistics rows of
+ * radamw_fused_step_multi and their coarse indexes.  The device tables, the
+ * statistics rows and the merge scratch live in one device allocation the
+ * list owns, so a step only launches.  The arithmetic, the launch policy and
+ * every result are those of radamw_step_multi / radamw_step_multi_writeback
+ * / radamw_fused_step_multi on the same segments, bit for bit.
+ *
+ * OWNERSHIP (the one exception to "the library keeps no pointer"): a list
+ * keeps the segment and model-copy pointers it was created with.  The
+ * caller keeps every one of those buffers allocated, at the same address
+ * and size, until radamw_list_destroy; stepping a list whose buffers were
+ * freed or moved is undefined (the kernels would touch freed memory).  A
+ * gradient that moves to a new buffer needs a new list.
+ *
+ * radamw_list_create(segs, nseg, gdt, amsgrad, models, model_dtype, stream,
+ *                    list_out)
+ *   segs, nseg, gdt : as radamw_step_multi (host array, device buffers,
+ *                     in place); validated here exactly as there, with the
+ *                     AMSGrad flag `amsgrad` (0/1) fixed for the list.
+ *   models          : host array of nseg device pointers to FP16 / BF16
+ *                     model copies (entries may be NULL), or NULL for none;
+ *                     model_dtype is then RADAMW_F16 or RADAMW_BF16.
+ *   stream          : fixes the device; the tables are uploaded on it and
+ *                     the call synchronises it once.
+ *   list_out        : host; receives the handle.  Allocates device memory
+ *                     (tables + 12 B per statistics row + merge scratch).
+ *   Errors as radamw_step_multi, plus RADAMW_ERR_RANGE when the rows exceed
+ *   the merge plan's limit.  On error nothing is allocated.
+ *
+ * radamw_list_step(list, step, opts, ctrl, stream, updated)
+ *   radamw_step_multi (or the write-back variant, when the list has model
+ *   copies) over the list's segments.  opts->amsgrad must equal the list's
+ *   flag (RADAMW_ERR_STATE otherwise); the stream must be on the list's
+ *   device (RADAMW_ERR_INVALID otherwise).
+ *
+ * radamw_list_fused_step(list, step, opts, gradient_scale, max_grad_norm,
+ *                        hierarchical, stream, result)
+ *   radamw_fused_step_multi over the list's segments, using the list's own
+ *   rows and scratch as the workspace.  Synchronises the stream once (the
+ *   report read-back).
+ *
+ * Calls on one list serialise on a lock inside it; calls on different
+ * lists are independent.  radamw_time_next_update applies to the update
+ * launches of a list step as to radamw_step_multi's.
+ *
+ * radamw_list_destroy(list): waits for the last submitted kernel that reads
+ * the list's device memory, frees it and the handle.  NULL is accepted.
+ */
+typedef struct radamw_list_s *radamw_list;
+
+int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt,
+                       int32_t amsgrad, void *const *models, radamw_dtype model_dtype,
+                       radamw_stream_t stream, radamw_list *list_out);
+int radamw_list_step(radamw_list list, uint64_t *step, const radamw_options *opts,
+                     const radamw_control *ctrl, radamw_stream_t stream, int32_t *updated);
+int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_options *opts,
+                           double gradient_scale, double max_grad_norm,
+                           int32_t hierarchical, radamw_stream_t stream,
+                           radamw_fused_result *result);
+int radamw_list_destroy(radamw_list list);
+
+/*
  * The FP32 constants one update launches with, formed on the host in FP64
  * and cast (FA-ja "この演算子を使用する理由": bias corrections by an FP64
  * integer power, cast to FP32), for update number t >= 1:
@@ -357,10 +427,11 @@ uint64_t radamw_launch_count(void);
 
 /*
  * Measurement hook (not part of the method): the next radamw_step,
- * radamw_step_inplace, radamw_step_multi or radamw_fused_step_multi call on
- * this thread that launches an update records start_event when its first
- * update kernel starts and stop_event when its last update kernel ends
- * (hipExtLaunchKernelGGL), so the host's submission latency is not timed.
+ * radamw_step_inplace, radamw_step_multi, radamw_fused_step_multi or list
+ * step call on this thread that launches an update records start_event
+ * when its first update kernel starts and stop_event when its last update
+ * kernel ends (hipExtLaunchKernelGGL), so the host's submission latency is
+ * not timed.
  * The events are caller-created hipEvent_t of the stream's device; passing
  * NULL, NULL clears the request.  Always returns RADAMW_OK.
  */

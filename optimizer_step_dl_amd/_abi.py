@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from dataclasses import dataclass, field
 from typing import Optional, Sequence
 
@@ -152,6 +153,10 @@ def load(path: str = LIB_PATH):
         "radamw_last_hip_error": ([], ctypes.c_int),
         "radamw_launch_count": ([], u64),
         "radamw_time_next_update": ([vp, vp], ctypes.c_int),
+        "radamw_list_create": ([P(_Segment), i32, i32, i32, P(vp), i32, vp, P(vp)], ctypes.c_int),
+        "radamw_list_step": ([vp, P(u64), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
+        "radamw_list_fused_step": ([vp, P(u64), P(Options), dbl, dbl, i32, vp, P(FusedResult)], ctypes.c_int),
+        "radamw_list_destroy": ([vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -166,7 +171,8 @@ EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "rada
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
-           "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update")
+           "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update",
+           "radamw_list_create", "radamw_list_step", "radamw_list_fused_step", "radamw_list_destroy")
 
 
 # ----------------------------------------------------------------- helpers --
@@ -366,6 +372,22 @@ def radamw_step_multi(segments, step: int, opts: Options, ctrl: Control):
     return bool(updated.value), int(st.value)
 
 
+def _models(models, segs, dev):
+    """Host array of model-copy pointers (None entries stay NULL) and their
+    shared dtype."""
+    mdt = None
+    ptrs = (ctypes.c_void_p * max(1, len(segs)))()
+    for i, (m, s) in enumerate(zip(models, segs)):
+        if m is None:
+            continue
+        _dense(m, f"model copy {i}", numel=s.param.numel(), device=dev)
+        if m.dtype not in (torch.float16, torch.bfloat16) or (mdt is not None and m.dtype != mdt):
+            raise ValueError("model copies must all be float16 or all bfloat16")
+        mdt = m.dtype
+        ptrs[i] = m.data_ptr()
+    return ptrs, mdt
+
+
 def radamw_step_multi_writeback(segments, models: Sequence[Optional[torch.Tensor]], step: int, opts: Options,
                                 ctrl: Control):
     """radamw_step_multi plus a 16-bit model copy per tensor, written in the
@@ -376,16 +398,7 @@ def radamw_step_multi_writeback(segments, models: Sequence[Optional[torch.Tensor
     if len(models) != count:
         raise ValueError("one model entry (tensor or None) per segment")
     segs = segments.segments if isinstance(segments, SegmentList) else segments
-    mdt = None
-    ptrs = (ctypes.c_void_p * max(1, count))()
-    for i, (m, s) in enumerate(zip(models, segs)):
-        if m is None:
-            continue
-        _dense(m, f"model copy {i}", numel=s.param.numel(), device=dev)
-        if m.dtype not in (torch.float16, torch.bfloat16) or (mdt is not None and m.dtype != mdt):
-            raise ValueError("model copies must all be float16 or all bfloat16")
-        mdt = m.dtype
-        ptrs[i] = m.data_ptr()
+    ptrs, mdt = _models(models, segs, dev)
     st = ctypes.c_uint64(step)
     updated = ctypes.c_int32(0)
     with torch.cuda.device(dev):
@@ -489,6 +502,100 @@ def radamw_fused_step_multi(segments, step: int, opts: Options,
             _stream(dev), ctypes.byref(res))
     _check(rc, "radamw_fused_step_multi")
     return res, int(st.value)
+
+
+class TensorList:
+    """A persistent tensor list (radamw_list_create): the segments are
+    validated once and their launch tables kept in device memory, so each
+    step only launches.  The list holds a reference to every tensor it was
+    built from, so their storage stays allocated while it lives; a gradient
+    that moves to a new tensor needs a new list.  ``models`` optionally
+    gives a float16 / bfloat16 model copy per segment (or None), rewritten
+    by every update.  Free it with close() (or a ``with`` block)."""
+
+    def __init__(self, segments, amsgrad: bool, models: Optional[Sequence[Optional[torch.Tensor]]] = None):
+        lib = load()
+        self.segments = list(segments.segments if isinstance(segments, SegmentList) else segments)
+        arr, code, dev = _segments(self.segments, False)
+        self.device, self.code, self.amsgrad = dev, code, bool(amsgrad)
+        self.models = None if models is None else list(models)
+        ptrs, mdt = None, None
+        if self.models is not None:
+            if len(self.models) != len(self.segments):
+                raise ValueError("one model entry (tensor or None) per segment")
+            ptrs, mdt = _models(self.models, self.segments, dev)
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(dev):
+            rc = lib.radamw_list_create(arr, len(self.segments), code, int(self.amsgrad), ptrs,
+                                        _DTYPE_CODE[mdt or torch.bfloat16], _stream(dev), ctypes.byref(handle))
+        _check(rc, "radamw_list_create")
+        self._handle = handle
+
+    def _live(self):
+        if self._handle is None:
+            raise RuntimeError("the tensor list was closed")
+        return self._handle
+
+    def step(self, step: int, opts: Options, ctrl: Control):
+        """radamw_step_multi over the list.  Returns (updated, new_step)."""
+        st = ctypes.c_uint64(step)
+        updated = ctypes.c_int32(0)
+        with torch.cuda.device(self.device):
+            rc = load().radamw_list_step(self._live(), ctypes.byref(st), ctypes.byref(opts), ctypes.byref(ctrl),
+                                         _stream(self.device), ctypes.byref(updated))
+        _check(rc, "radamw_list_step")
+        return bool(updated.value), int(st.value)
+
+    def fused_step(self, step: int, opts: Options, gradient_scale: float, max_grad_norm: Optional[float],
+                   hierarchical: bool):
+        """radamw_fused_step_multi over the list.  Returns (FusedResult, new_step)."""
+        st = ctypes.c_uint64(step)
+        res = FusedResult()
+        with torch.cuda.device(self.device):
+            rc = load().radamw_list_fused_step(self._live(), ctypes.byref(st), ctypes.byref(opts),
+                                               float(gradient_scale),
+                                               0.0 if max_grad_norm is None else float(max_grad_norm),
+                                               int(bool(hierarchical)), _stream(self.device), ctypes.byref(res))
+        _check(rc, "radamw_list_fused_step")
+        return res, int(st.value)
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None:
+            h, self._handle = self._handle, None
+            _check(load().radamw_list_destroy(h), "radamw_list_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        if getattr(self, "_handle", None) is not None and not sys.is_finalizing():
+            try:
+                self.close()
+            except Exception:
+                pass
+
+    def __len__(self):
+        return len(self.segments)
+
+
+def radamw_list_create(segments, amsgrad: bool, models=None) -> TensorList:
+    return TensorList(segments, amsgrad, models)
+
+
+def radamw_list_step(lst: TensorList, step: int, opts: Options, ctrl: Control):
+    return lst.step(step, opts, ctrl)
+
+
+def radamw_list_fused_step(lst: TensorList, step: int, opts: Options, gradient_scale: float,
+                           max_grad_norm: Optional[float], hierarchical: bool):
+    return lst.fused_step(step, opts, gradient_scale, max_grad_norm, hierarchical)
+
+
+def radamw_list_destroy(lst: TensorList) -> None:
+    lst.close()
 
 
 def radamw_host_coefficients(opts: Options, t: int, gradient_scale: float = 1.0) -> list[float]:

@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -346,10 +347,16 @@ int staged_launch(int dev, hipStream_t stream, size_t bytes, Fill fill, Launch l
     return RADAMW_OK;
 }
 
-// Several tensors in one launch: descriptors, tile prefix sums and the
-// coarse index go through a staged table (staged_launch).
-int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
-                 int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+// The device table of a multi-tensor update launch: descriptors, tile
+// prefix sums and a coarse index, packed into one byte image.
+struct UpdateTable {
+    std::vector<char> bytes;
+    size_t prefix_off = 0, coarse_off = 0;
+    int32_t nseg = 0;
+    int64_t tiles = 0;
+};
+
+int build_update_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, UpdateTable *t) {
     const int32_t nseg = static_cast<int32_t>(segs.size());
     std::vector<int64_t> prefix(nseg + 1);
     int64_t tiles = 0;
@@ -360,6 +367,7 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
         tiles += segment_tiles(segs[i].n, segs[i].head);
     }
     prefix[nseg] = tiles;
+    if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
     // coarse[j] = the (non-empty) segment holding tile j << TABLE_COARSE_LOG2;
     // the last entry closes the range with the last segment.
     const int64_t ncoarse = ((tiles - 1) >> TABLE_COARSE_LOG2) + 1;
@@ -367,8 +375,8 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     {
         int32_t s = 0;
         for (int64_t j = 0; j < ncoarse; ++j) {
-            const int64_t t = j << TABLE_COARSE_LOG2;
-            while (prefix[s + 1] <= t) ++s;
+            const int64_t tile = j << TABLE_COARSE_LOG2;
+            while (prefix[s + 1] <= tile) ++s;
             coarse[j] = s;
         }
         coarse[ncoarse] = nseg - 1;
@@ -376,47 +384,56 @@ int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, 
     const size_t desc_bytes = sizeof(SegDesc) * nseg;
     const size_t prefix_bytes = sizeof(int64_t) * (nseg + 1);
     const size_t coarse_bytes = sizeof(int32_t) * (ncoarse + 1);
-    const size_t bytes = desc_bytes + prefix_bytes + coarse_bytes;
-    if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
-    const int grid = update_grid(tiles);
+    t->bytes.resize(desc_bytes + prefix_bytes + coarse_bytes);
+    t->prefix_off = desc_bytes;
+    t->coarse_off = desc_bytes + prefix_bytes;
+    std::memcpy(t->bytes.data(), segs.data(), desc_bytes);
+    std::memcpy(t->bytes.data() + t->prefix_off, prefix.data(), prefix_bytes);
+    std::memcpy(t->bytes.data() + t->coarse_off, coarse.data(), coarse_bytes);
+    t->nseg = nseg;
+    t->tiles = tiles;
+    return RADAMW_OK;
+}
+
+// Launch an update over a table already in device memory at `base`.
+hipError_t launch_table_at(const UpdateTable &t, const char *base, int gdt, bool amsgrad, bool first,
+                           const Coefs &c, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    return launch_update_table(reinterpret_cast<const SegDesc *>(base),
+                               reinterpret_cast<const int64_t *>(base + t.prefix_off),
+                               reinterpret_cast<const int32_t *>(base + t.coarse_off), t.nseg, t.tiles, c, gdt,
+                               amsgrad, first, update_grid(t.tiles), stream, ev_start, ev_stop);
+}
+
+// Several tensors in one launch, the table going through a staged slot
+// (staged_launch).
+int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
+                 int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    UpdateTable t;
+    int rc = build_update_table(segs, gdt, amsgrad, first, &t);
+    if (rc) return rc;
     return staged_launch(
-        dev, stream, bytes,
-        [&](char *host) {
-            std::memcpy(host, segs.data(), desc_bytes);
-            std::memcpy(host + desc_bytes, prefix.data(), prefix_bytes);
-            std::memcpy(host + desc_bytes + prefix_bytes, coarse.data(), coarse_bytes);
-        },
+        dev, stream, t.bytes.size(), [&](char *host) { std::memcpy(host, t.bytes.data(), t.bytes.size()); },
         [&](const char *dev_base) {
-            const SegDesc *d_segs = reinterpret_cast<const SegDesc *>(dev_base);
-            const int64_t *d_prefix = reinterpret_cast<const int64_t *>(dev_base + desc_bytes);
-            const int32_t *d_coarse = reinterpret_cast<const int32_t *>(dev_base + desc_bytes + prefix_bytes);
-            return launch_update_table(d_segs, d_prefix, d_coarse, nseg, tiles, c, gdt, amsgrad, first, grid,
-                                       stream, ev_start, ev_stop);
+            return launch_table_at(t, dev_base, gdt, amsgrad, first, c, stream, ev_start, ev_stop);
         });
 }
 
-// Validated multi-tensor update (shared by radamw_step_multi, the write-back
-// variant and the fused step).  models (optional) holds a 16-bit model copy
-// per segment (entries may be null), of dtype model_dtype.
-int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *step,
-                 const radamw_options &o, double gradient_scale, int dev, hipStream_t stream,
-                 int32_t *updated, void *const *models = nullptr, int model_dtype = 0) {
+// In-place descriptors of the non-empty segments of a list; models
+// (optional) holds a 16-bit model copy per segment (entries may be null), of
+// dtype model_dtype.
+std::vector<SegDesc> inplace_descs(const radamw_segment *segs, int32_t nseg, void *const *models,
+                                   int model_dtype) {
     std::vector<SegDesc> active;
-    active.reserve(nseg);
-    const bool first = (*step == 0);
+    active.reserve(static_cast<size_t>(nseg));
     for (int32_t i = 0; i < nseg; ++i) {
         const radamw_segment &s = segs[i];
         if (s.n == 0) continue;
         SegDesc d{};
-        d.p_in = s.param;
+        d.p_in = d.p_out = s.param;
         d.g = s.grad;
-        d.m_in = s.exp_avg;
-        d.v_in = s.exp_avg_sq;
-        d.vmax_in = s.max_exp_avg_sq;
-        d.p_out = s.param;
-        d.m_out = s.exp_avg;
-        d.v_out = s.exp_avg_sq;
-        d.vmax_out = s.max_exp_avg_sq;
+        d.m_in = d.m_out = s.exp_avg;
+        d.v_in = d.v_out = s.exp_avg_sq;
+        d.vmax_in = d.vmax_out = s.max_exp_avg_sq;
         d.n = s.n;
         if (models && models[i]) {
             d.model = models[i];
@@ -424,18 +441,23 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
         }
         active.push_back(d);
     }
-    if (active.empty()) {
-        *updated = 0;
-        return RADAMW_OK;
-    }
-    const Coefs c = make_coefs(o, *step + 1, gradient_scale);
-    const bool ams = o.amsgrad != 0;
-    // Launch policy: a tensor of at least MULTI_SOLO_MIN elements gets a
-    // launch of its own; all smaller tensors share one launch.
-    std::vector<SegDesc> solo, shared;
+    return active;
+}
+
+// Launch policy: a tensor of at least MULTI_SOLO_MIN elements gets a launch
+// of its own; all smaller tensors share one launch.
+void split_launches(const std::vector<SegDesc> &active, std::vector<SegDesc> &solo, std::vector<SegDesc> &shared) {
     for (const SegDesc &d : active) (d.n >= MULTI_SOLO_MIN ? solo : shared).push_back(d);
+}
+
+// Submit the update launches of one step: every solo tensor, then the
+// shared ones in one launch, whose table is either staged now or already
+// resident in device memory (resident != null: its image and device base).
+// Measurement events, if requested, go on the first and the last launch.
+int submit_updates(const std::vector<SegDesc> &solo, std::vector<SegDesc> &shared, const UpdateTable *resident,
+                   const char *resident_base, int gdt, bool ams, bool first, const Coefs &c, int dev,
+                   hipStream_t stream) {
     const size_t launches = solo.size() + (shared.empty() ? 0 : 1);
-    // measurement events, if requested: start on the first launch, stop on the last
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
     size_t k = 0;
@@ -446,8 +468,31 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
         if ((rc = launch_single(d, gdt, ams, first, c, dev, stream, ev_start(), ev_stop()))) return rc;
         ++k;
     }
-    if (shared.size() == 1) rc = launch_single(shared[0], gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
-    else if (shared.size() > 1) rc = launch_table(shared, gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+    if (shared.size() == 1) {
+        rc = launch_single(shared[0], gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+    } else if (shared.size() > 1 && resident) {
+        rc = hip_status(launch_table_at(*resident, resident_base, gdt, ams, first, c, stream, ev_start(), ev_stop()));
+        if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
+    } else if (shared.size() > 1) {
+        rc = launch_table(shared, gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+    }
+    return rc;
+}
+
+// Validated multi-tensor update (shared by radamw_step_multi, the write-back
+// variant and the fused step).
+int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *step,
+                 const radamw_options &o, double gradient_scale, int dev, hipStream_t stream,
+                 int32_t *updated, void *const *models = nullptr, int model_dtype = 0) {
+    std::vector<SegDesc> active = inplace_descs(segs, nseg, models, model_dtype);
+    if (active.empty()) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    const Coefs c = make_coefs(o, *step + 1, gradient_scale);
+    std::vector<SegDesc> solo, shared;
+    split_launches(active, solo, shared);
+    const int rc = submit_updates(solo, shared, nullptr, nullptr, gdt, o.amsgrad != 0, *step == 0, c, dev, stream);
     if (rc != RADAMW_OK) return rc;
     *step += 1;
     *updated = 1;
@@ -558,6 +603,142 @@ void decode(const radamw_stats &r, double *sumsq, uint32_t *count) {
     const uint64_t bits = uint64_t(r.w[0]) | (uint64_t(r.w[1]) << 32);
     std::memcpy(sumsq, &bits, sizeof(double));
     *count = r.w[2];
+}
+
+// The statistics rows of a list of non-empty gradients, packed back to back
+// (the same records per-tensor launches would write).
+std::vector<StatsSeg> stats_segments(const radamw_segment *segs, int32_t nseg, int gdt, int64_t *nrows_out) {
+    std::vector<StatsSeg> st;
+    st.reserve(static_cast<size_t>(nseg));
+    int64_t nrows = 0;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const radamw_segment &s = segs[i];
+        if (s.n == 0) continue;
+        const int64_t r = stats_rows(s.n, gdt);
+        st.push_back(StatsSeg{s.grad, s.n, nrows, stats_head(s.grad, gdt, s.n), static_cast<int32_t>(r)});
+        nrows += r;
+    }
+    *nrows_out = nrows;
+    return st;
+}
+
+// Device image of a multi-tensor statistics launch: the StatsSeg array,
+// then coarse[j] = the gradient holding row j << STATS_COARSE_LOG2 (the last
+// entry closes the range with the last gradient).
+std::vector<char> build_stats_table(const std::vector<StatsSeg> &st, int64_t nrows, size_t *coarse_off) {
+    const int32_t ns = static_cast<int32_t>(st.size());
+    const int64_t ncoarse = ((nrows - 1) >> STATS_COARSE_LOG2) + 1;
+    std::vector<int32_t> coarse(ncoarse + 1);
+    int32_t k = 0;
+    for (int64_t j = 0; j < ncoarse; ++j) {
+        const int64_t r = j << STATS_COARSE_LOG2;
+        while (k + 1 < ns && st[k + 1].row_begin <= r) ++k;
+        coarse[j] = k;
+    }
+    coarse[ncoarse] = ns - 1;
+    const size_t seg_bytes = sizeof(StatsSeg) * st.size();
+    std::vector<char> bytes(seg_bytes + sizeof(int32_t) * coarse.size());
+    std::memcpy(bytes.data(), st.data(), seg_bytes);
+    std::memcpy(bytes.data() + seg_bytes, coarse.data(), sizeof(int32_t) * coarse.size());
+    *coarse_off = seg_bytes;
+    return bytes;
+}
+
+// Merge the rows and read the 12-byte report back: the final merge writes
+// straight into host memory mapped for the device, so the stream
+// synchronisation is the read-back.
+int report_to_host(const StatsRec *rows, int64_t nrows, StatsRec *scratch, bool hierarchical, int dev,
+                   hipStream_t stream, radamw_stats *host) {
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.report_mu);
+    if (!dc.mapped_report_host) {
+        void *hp = nullptr, *dp = nullptr;
+        hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
+        if (e != hipSuccess) return hip_status(e);
+        e = hipHostGetDevicePointer(&dp, hp, 0);
+        if (e != hipSuccess) {
+            (void)hipHostFree(hp);
+            return hip_status(e);
+        }
+        dc.mapped_report_host = static_cast<radamw_stats *>(hp);
+        dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
+    }
+    StatsRec *mapped = reinterpret_cast<StatsRec *>(dc.mapped_report_dev);
+    int rc = merge_launch(rows, nrows, scratch, mapped, hierarchical, stream);
+    if (rc) return rc;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    std::memcpy(host, dc.mapped_report_host, sizeof *host);
+    return RADAMW_OK;
+}
+
+}  // namespace
+
+// ========================================================= tensor lists ==
+
+// A validated tensor list kept across steps: the launch split, the update
+// descriptors and the statistics rows are computed once, and the device
+// tables (plus the statistics rows and merge scratch) live in one device
+// allocation the list owns.  Steps on one list serialise on its mutex.
+struct radamw_list_s {
+    std::mutex mu;
+    int dev = 0;
+    int gdt = 0;
+    bool amsgrad = false;
+    int64_t active = 0;
+    std::vector<SegDesc> solo, shared;
+    UpdateTable table;        // image of the shared launch's table (shared.size() > 1)
+    std::vector<StatsSeg> st; // statistics rows of the non-empty gradients
+    int64_t nrows = 0;
+    size_t stats_coarse_off = 0;
+    char *mem = nullptr;      // device: [update table][stats table][rows][merge scratch]
+    size_t table_off = 0, stats_off = 0, rows_off = 0;
+    hipEvent_t done = nullptr;  // recorded after the last launch that reads `mem`
+    bool pending = false;
+};
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Temporarily make `dev` the calling thread's current device.
+struct DeviceScope {
+    int prev = -1;
+    explicit DeviceScope(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) (void)hipSetDevice(dev);
+    }
+    ~DeviceScope() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+// Checks shared by the list's step entry points.
+int list_step_checks(radamw_list_s *l, const radamw_options *opts, const uint64_t *step, hipStream_t stream) {
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if (!l || !step) return RADAMW_ERR_INVALID;
+    if ((opts->amsgrad != 0) != l->amsgrad) return RADAMW_ERR_STATE;
+    if (*step == UINT64_MAX) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    if (dev != l->dev) return RADAMW_ERR_INVALID;
+    return RADAMW_OK;
+}
+
+// The update launches of one list step, then the event that guards `mem`.
+int list_update(radamw_list_s *l, uint64_t *step, const radamw_options &o, double gradient_scale,
+                hipStream_t stream) {
+    const Coefs c = make_coefs(o, *step + 1, gradient_scale);
+    int rc = submit_updates(l->solo, l->shared, l->shared.size() > 1 ? &l->table : nullptr, l->mem + l->table_off,
+                            l->gdt, l->amsgrad, *step == 0, c, l->dev, stream);
+    if (rc) return rc;
+    hipError_t e = hipEventRecord(l->done, stream);
+    if (e != hipSuccess) return hip_status(e);
+    l->pending = true;
+    *step += 1;
+    return RADAMW_OK;
 }
 
 }  // namespace
@@ -921,60 +1102,25 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     // launch (the same records per-tensor launches would write)
     StatsRec *rows = static_cast<StatsRec *>(workspace);
     int64_t nrows = 0;
-    std::vector<StatsSeg> st;
-    st.reserve(static_cast<size_t>(active));
-    for (int32_t i = 0; i < nseg; ++i) {
-        const radamw_segment &s = segs[i];
-        if (s.n == 0) continue;
-        const int64_t r = stats_rows(s.n, gdt);
-        st.push_back(StatsSeg{s.grad, s.n, nrows, stats_head(s.grad, gdt, s.n), static_cast<int32_t>(r)});
-        nrows += r;
-    }
+    const std::vector<StatsSeg> st = stats_segments(segs, nseg, gdt, &nrows);
     if (st.size() == 1) {
         rc = hip_status(launch_analyze(st[0].g, gdt, st[0].n, st[0].head, st[0].rows, rows, stream));
         if (rc) return rc;
         g_launches.fetch_add(1, std::memory_order_relaxed);
     } else {
-        const size_t bytes = sizeof(StatsSeg) * st.size();
+        size_t coarse_off = 0;
+        const std::vector<char> table = build_stats_table(st, nrows, &coarse_off);
         rc = staged_launch(
-            dev, stream, bytes, [&](char *host) { std::memcpy(host, st.data(), bytes); },
+            dev, stream, table.size(), [&](char *host) { std::memcpy(host, table.data(), table.size()); },
             [&](const char *dev_base) {
                 return launch_analyze_table(reinterpret_cast<const StatsSeg *>(dev_base),
-                                            static_cast<int32_t>(st.size()), nrows, gdt, rows, stream);
+                                            reinterpret_cast<const int32_t *>(dev_base + coarse_off), nrows, gdt,
+                                            rows, stream);
             });
         if (rc) return rc;
     }
-    int64_t se;
-    int32_t ex;
-    plan(nrows, &se, &ex);
-    StatsRec *scratch = rows + nrows;
-    StatsRec *report = scratch + se / 3;  // reserved in the workspace layout
-
-    (void)report;
     radamw_stats host;
-    {
-        // the final merge writes straight into mapped host memory; the
-        // stream synchronisation is the read-back
-        DeviceCache &dc = g_devices[dev];
-        std::lock_guard<std::mutex> lock(dc.report_mu);
-        if (!dc.mapped_report_host) {
-            void *hp = nullptr, *dp = nullptr;
-            hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
-            if (e != hipSuccess) return hip_status(e);
-            e = hipHostGetDevicePointer(&dp, hp, 0);
-            if (e != hipSuccess) {
-                (void)hipHostFree(hp);
-                return hip_status(e);
-            }
-            dc.mapped_report_host = static_cast<radamw_stats *>(hp);
-            dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
-        }
-        StatsRec *mapped = reinterpret_cast<StatsRec *>(dc.mapped_report_dev);
-        if ((rc = merge_launch(rows, nrows, scratch, mapped, hierarchical != 0, stream))) return rc;
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_status(e);
-        std::memcpy(&host, dc.mapped_report_host, sizeof host);
-    }
+    if ((rc = report_to_host(rows, nrows, rows + nrows, hierarchical != 0, dev, stream, &host))) return rc;
     radamw_control ctrl;
     radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
     if (ctrl.skip_update) {
@@ -986,6 +1132,145 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     if (rc) return rc;
     result->updated = updated;
     return RADAMW_OK;
+}
+
+int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, int32_t amsgrad,
+                       void *const *models, radamw_dtype model_dtype, radamw_stream_t stream_,
+                       radamw_list *list_out) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!list_out || nseg < 0 || (nseg > 0 && !segs) || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
+    if (amsgrad != 0 && amsgrad != 1) return RADAMW_ERR_INVALID;
+    if (models && model_dtype != RADAMW_F16 && model_dtype != RADAMW_BF16) return RADAMW_ERR_INVALID;
+    for (int32_t i = 0; i < nseg; ++i)
+        if (segs[i].n < 0) return RADAMW_ERR_INVALID;
+    int rc, dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    int64_t active = 0;
+    if ((rc = check_segments(segs, nseg, gdt, amsgrad != 0, false, dev, &active, models))) return rc;
+
+    std::unique_ptr<radamw_list_s> l(new radamw_list_s);
+    l->dev = dev;
+    l->gdt = gdt;
+    l->amsgrad = amsgrad != 0;
+    l->active = active;
+    std::vector<SegDesc> descs = inplace_descs(segs, nseg, models, model_dtype);
+    split_launches(descs, l->solo, l->shared);
+    // heads of an in-place update do not depend on the step, so one table
+    // serves the first step and every later one
+    if (l->shared.size() > 1 && (rc = build_update_table(l->shared, gdt, l->amsgrad, false, &l->table))) return rc;
+    l->st = stats_segments(segs, nseg, gdt, &l->nrows);
+    int64_t se = 0;
+    int32_t ex = 0;
+    if (l->nrows > 0 && (rc = plan(l->nrows, &se, &ex))) return rc;
+    std::vector<char> stats_table;
+    if (l->st.size() > 1) stats_table = build_stats_table(l->st, l->nrows, &l->stats_coarse_off);
+
+    l->table_off = 0;
+    l->stats_off = align_up(l->table.bytes.size(), 256);
+    l->rows_off = align_up(l->stats_off + stats_table.size(), 256);
+    const size_t total = l->rows_off + static_cast<size_t>(l->nrows) * 12 + static_cast<size_t>(se) * 4;
+    DeviceScope scope(dev);
+    if (total > 0) {
+        hipError_t e = hipMalloc(&l->mem, total);
+        if (e != hipSuccess) {
+            l->mem = nullptr;
+            return hip_status(e);
+        }
+    }
+    auto fail = [&](hipError_t e) {
+        (void)hipFree(l->mem);
+        if (l->done) (void)hipEventDestroy(l->done);
+        return hip_status(e);
+    };
+    hipError_t e = hipEventCreateWithFlags(&l->done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        l->done = nullptr;
+        return fail(e);
+    }
+    if (!l->table.bytes.empty() &&
+        (e = hipMemcpyAsync(l->mem + l->table_off, l->table.bytes.data(), l->table.bytes.size(),
+                            hipMemcpyHostToDevice, stream)) != hipSuccess)
+        return fail(e);
+    if (!stats_table.empty() &&
+        (e = hipMemcpyAsync(l->mem + l->stats_off, stats_table.data(), stats_table.size(), hipMemcpyHostToDevice,
+                            stream)) != hipSuccess)
+        return fail(e);
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return fail(e);
+    *list_out = l.release();
+    return RADAMW_OK;
+}
+
+int radamw_list_step(radamw_list list, uint64_t *step, const radamw_options *opts, const radamw_control *ctrl,
+                     radamw_stream_t stream_, int32_t *updated) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_control(ctrl))) return rc;
+    if (!updated) return RADAMW_ERR_INVALID;
+    if ((rc = list_step_checks(list, opts, step, stream))) return rc;
+    std::lock_guard<std::mutex> lock(list->mu);
+    if (ctrl->skip_update || list->active == 0) {
+        *updated = 0;
+        return RADAMW_OK;
+    }
+    if ((rc = list_update(list, step, *opts, ctrl->gradient_scale, stream))) return rc;
+    *updated = 1;
+    return RADAMW_OK;
+}
+
+int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_options *opts, double gradient_scale,
+                           double max_grad_norm, int32_t hierarchical, radamw_stream_t stream_,
+                           radamw_fused_result *result) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    if (!result || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    if (hierarchical != 0 && hierarchical != 1) return RADAMW_ERR_INVALID;
+    if ((rc = list_step_checks(list, opts, step, stream))) return rc;
+    std::lock_guard<std::mutex> lock(list->mu);
+    std::memset(result, 0, sizeof *result);
+    result->clip_coef = 1.0;
+    if (list->active == 0) return RADAMW_OK;
+    StatsRec *rows = reinterpret_cast<StatsRec *>(list->mem + list->rows_off);
+    if (list->st.size() == 1) {
+        const StatsSeg &g = list->st[0];
+        rc = hip_status(launch_analyze(g.g, list->gdt, g.n, g.head, g.rows, rows, stream));
+    } else {
+        const char *base = list->mem + list->stats_off;
+        rc = hip_status(launch_analyze_table(reinterpret_cast<const StatsSeg *>(base),
+                                             reinterpret_cast<const int32_t *>(base + list->stats_coarse_off),
+                                             list->nrows, list->gdt, rows, stream));
+    }
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    radamw_stats host;
+    if ((rc = report_to_host(rows, list->nrows, rows + list->nrows, hierarchical != 0, list->dev, stream, &host)))
+        return rc;
+    radamw_control ctrl;
+    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
+    if (ctrl.skip_update) {
+        result->updated = 0;
+        return RADAMW_OK;
+    }
+    if ((rc = list_update(list, step, *opts, ctrl.gradient_scale, stream))) return rc;
+    result->updated = 1;
+    return RADAMW_OK;
+}
+
+int radamw_list_destroy(radamw_list list) {
+    if (!list) return RADAMW_OK;
+    int rc = RADAMW_OK;
+    {
+        std::lock_guard<std::mutex> lock(list->mu);
+        DeviceScope scope(list->dev);
+        if (list->pending) {
+            hipError_t e = hipEventSynchronize(list->done);
+            if (e != hipSuccess) rc = hip_status(e);
+        }
+        if (list->mem) (void)hipFree(list->mem);
+        if (list->done) (void)hipEventDestroy(list->done);
+    }
+    delete list;
+    return rc;
 }
 
 const char *radamw_status_string(int status) {

@@ -37,6 +37,9 @@ constexpr int64_t MULTI_SOLO_MIN = int64_t(1) << 22;
 // Coarse index of the multi-tensor kernel: one entry per 2^10 tiles
 // (256K elements), naming the segment that holds that tile.
 constexpr int TABLE_COARSE_LOG2 = 10;
+// A multi-tensor statistics launch indexes its rows the same way: coarse
+// entry j names the gradient holding row j << STATS_COARSE_LOG2.
+constexpr int STATS_COARSE_LOG2 = 8;
 
 // Grid of the update kernels: exactly one workgroup per tile.  A launch may
 // hold at most this many tiles (~5.5e11 elements, far beyond device memory).
@@ -149,8 +152,8 @@ hipError_t launch_staged(float *p, const void *g, int gdt, float *m, float *v, f
                          int64_t n, bool first, const Coefs &c, hipStream_t stream, int *launched);
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream);
-hipError_t launch_analyze_table(const StatsSeg *segs_dev, int32_t nseg, int64_t total_rows, int gdt,
-                                StatsRec *out, hipStream_t stream);
+hipError_t launch_analyze_table(const StatsSeg *segs_dev, const int32_t *coarse_dev, int64_t total_rows,
+                                int gdt, StatsRec *out, hipStream_t stream);
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
                         StatsRec *out, hipStream_t stream);
 

@@ -191,13 +191,19 @@ __global__ __launch_bounds__(STATS_BLOCK) void grad_analyze(const void *g, int64
 }
 
 // Several gradients in one launch: workgroup b finds the gradient whose
-// records include b (binary search over row_begin) and computes the same
-// record a single-tensor launch would, so the reports are bit-identical.
+// records include b and computes the same record a single-tensor launch
+// would, so the reports are bit-identical.  coarse[j] is the gradient holding
+// row j << STATS_COARSE_LOG2, so the search runs over [coarse[j],
+// coarse[j + 1]] (usually one or two gradients) rather than the whole list:
+// a list of a few hundred tensors otherwise spends about as long in the
+// search's dependent loads as in streaming a 16 KiB row.
 template <int GDT>
 __global__ __launch_bounds__(STATS_BLOCK) void grad_analyze_table(const StatsSeg *__restrict__ segs,
-                                                                  int32_t nseg, StatsRec *out) {
+                                                                  const int32_t *__restrict__ coarse,
+                                                                  StatsRec *out) {
     const int64_t b = blockIdx.x;
-    int32_t lo = 0, hi = nseg;  // segs[lo].row_begin <= b < segs[hi].row_begin (hi == nseg: end)
+    const int64_t j = b >> STATS_COARSE_LOG2;
+    int32_t lo = coarse[j], hi = coarse[j + 1] + 1;  // segs[lo].row_begin <= b < segs[hi].row_begin
     while (hi - lo > 1) {
         const int32_t mid = (lo + hi) >> 1;
         if (segs[mid].row_begin <= b) lo = mid; else hi = mid;
@@ -240,13 +246,13 @@ hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64
     return hipGetLastError();
 }
 
-hipError_t launch_analyze_table(const StatsSeg *segs_dev, int32_t nseg, int64_t total_rows, int gdt,
-                                StatsRec *out, hipStream_t stream) {
+hipError_t launch_analyze_table(const StatsSeg *segs_dev, const int32_t *coarse_dev, int64_t total_rows,
+                                int gdt, StatsRec *out, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(total_rows)), block(STATS_BLOCK);
     switch (gdt) {
-    case G_F32: hipLaunchKernelGGL(grad_analyze_table<G_F32>, grid, block, 0, stream, segs_dev, nseg, out); break;
-    case G_F16: hipLaunchKernelGGL(grad_analyze_table<G_F16>, grid, block, 0, stream, segs_dev, nseg, out); break;
-    case G_BF16: hipLaunchKernelGGL(grad_analyze_table<G_BF16>, grid, block, 0, stream, segs_dev, nseg, out); break;
+    case G_F32: hipLaunchKernelGGL(grad_analyze_table<G_F32>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
+    case G_F16: hipLaunchKernelGGL(grad_analyze_table<G_F16>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
+    case G_BF16: hipLaunchKernelGGL(grad_analyze_table<G_BF16>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -181,3 +181,40 @@ def test_binding_rejects_host_and_strided_tensors(lib):
     with pytest.raises(ValueError):
         ra.radamw_step_inplace(p, torch.zeros(8), ra.AdamWState(0, torch.zeros(8), torch.zeros(8)),
                                ra.options(), ra.control())
+
+
+def test_list_entry_points_validate_before_any_device_call(lib):
+    """The persistent-list entry points reject bad arguments before the
+    library touches HIP; destroying NULL is a no-op."""
+    before = ra.radamw_launch_count()
+    out = ctypes.c_void_p()
+    seg = (_abi._Segment * 1)(_abi._Segment(None, None, None, None, None, 16))
+    bad_n = (_abi._Segment * 1)(_abi._Segment(None, None, None, None, None, -1))
+    models = (ctypes.c_void_p * 1)()
+    assert lib.radamw_list_create(seg, 1, 0, 0, None, 0, None, None) == -1          # no list_out
+    assert lib.radamw_list_create(seg, -1, 0, 0, None, 0, None, ctypes.byref(out)) == -1
+    assert lib.radamw_list_create(None, 2, 0, 0, None, 0, None, ctypes.byref(out)) == -1
+    assert lib.radamw_list_create(seg, 1, 7, 0, None, 0, None, ctypes.byref(out)) == -1  # dtype
+    assert lib.radamw_list_create(seg, 1, 0, 2, None, 0, None, ctypes.byref(out)) == -1  # amsgrad flag
+    assert lib.radamw_list_create(seg, 1, 0, 0, models, 0, None, ctypes.byref(out)) == -1  # FP32 copies
+    assert lib.radamw_list_create(bad_n, 1, 0, 0, None, 0, None, ctypes.byref(out)) == -1
+    assert out.value is None
+    step = ctypes.c_uint64(3)
+    upd = ctypes.c_int32(-7)
+    good = ra.options()
+    assert lib.radamw_list_step(None, ctypes.byref(step), ctypes.byref(good), ctypes.byref(ra.control()), None,
+                                ctypes.byref(upd)) == -1
+    assert lib.radamw_list_step(None, ctypes.byref(step), ctypes.byref(ra.options(lr=-1.0)),
+                                ctypes.byref(ra.control()), None, ctypes.byref(upd)) == -1
+    assert lib.radamw_list_step(None, ctypes.byref(step), ctypes.byref(good), ctypes.byref(ra.control(0.0)), None,
+                                ctypes.byref(upd)) == -1
+    res = _abi.FusedResult()
+    assert lib.radamw_list_fused_step(None, ctypes.byref(step), ctypes.byref(good), 1.0, 1.0, 1, None,
+                                      ctypes.byref(res)) == -1
+    assert lib.radamw_list_fused_step(None, ctypes.byref(step), ctypes.byref(good), float("nan"), 1.0, 1, None,
+                                      ctypes.byref(res)) == -1
+    assert lib.radamw_list_fused_step(None, ctypes.byref(step), ctypes.byref(good), 1.0, 1.0, 2, None,
+                                      ctypes.byref(res)) == -1
+    assert lib.radamw_list_destroy(None) == 0
+    assert step.value == 3 and upd.value == -7
+    assert ra.radamw_launch_count() == before

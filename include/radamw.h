@@ -365,8 +365,9 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
  *   models          : host array of nseg device pointers to FP16 / BF16
  *                     model copies (entries may be NULL), or NULL for none;
  *                     model_dtype is then RADAMW_F16 or RADAMW_BF16.
- *   stream          : fixes the device; the tables are uploaded on it and
- *                     the call synchronises it once.
+ *   stream          : fixes the device; the tables are uploaded on it
+ *                     from pinned memory the list keeps (the call does not
+ *                     wait for the stream).
  *   list_out        : host; receives the handle.  Allocates device memory
  *                     (tables + 12 B per statistics row + merge scratch).
  *   Errors as radamw_step_multi, plus RADAMW_ERR_RANGE when the rows exceed
@@ -384,8 +385,10 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
  *   rows and scratch as the workspace.  Synchronises the stream once (the
  *   report read-back).
  *
- * Calls on one list serialise on a lock inside it; calls on different
- * lists are independent.  radamw_time_next_update applies to the update
+ * Calls on one list serialise on a lock inside it, and each step's first
+ * kernel waits (hipStreamWaitEvent) for the list's previous work, the table
+ * upload or the last update, even when that went to another stream; calls
+ * on different lists are independent.  radamw_time_next_update applies to the update
  * launches of a list step as to radamw_step_multi's.
  *
  * radamw_list_destroy(list): waits for the last submitted kernel that reads
@@ -403,6 +406,38 @@ int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_option
                            int32_t hierarchical, radamw_stream_t stream,
                            radamw_fused_result *result);
 int radamw_list_destroy(radamw_list list);
+
+/*
+ * One fused step over several lists that take one decision together: the
+ * parameter groups of a torch optimizer (for example weights with weight
+ * decay and norms without), each with its own options and step count, under
+ * one global-norm clip and one non-finite skip (TR-zh "在 ruda:0 上进行原生
+ * PyTorch 训练": the statistics of every active group are reduced before any
+ * parameter is updated).
+ *
+ * radamw_lists_fused_step(lists, nlists, steps, opts, gradient_scale,
+ *                         max_grad_norm, hierarchical, stream, result)
+ *   lists  : host array of nlists distinct list handles (1..65536), all on
+ *            the stream's device.
+ *   steps  : host array of nlists completed-step counts, one per list; a
+ *            list that updates advances its own entry by one.
+ *   opts   : host array of nlists option structs; opts[k].amsgrad must
+ *            equal list k's flag.
+ *   Every list's gradients are analysed (one launch per list); each list's
+ *   rows are merged to one record (with the fan-in-1024 levels when
+ *   hierarchical = 1), and those records, in array order, take one final
+ *   merge into the report.  With a single non-empty list this is exactly
+ *   radamw_list_fused_step.  The decision is taken once on that report: a
+ *   non-finite value anywhere skips every list; otherwise every list
+ *   updates with the same clipped scale and its own options and step.
+ *   Lists with no non-empty tensor neither launch nor step.
+ *   Errors as radamw_list_fused_step, checked for every list before any
+ *   launch; a handle given twice is RADAMW_ERR_INVALID.
+ */
+int radamw_lists_fused_step(const radamw_list *lists, int32_t nlists, uint64_t *steps,
+                            const radamw_options *opts, double gradient_scale,
+                            double max_grad_norm, int32_t hierarchical,
+                            radamw_stream_t stream, radamw_fused_result *result);
 
 /*
  * The FP32 constants one update launches with, formed on the host in FP64

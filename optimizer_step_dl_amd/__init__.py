@@ -10,7 +10,7 @@ from ._abi import (  # noqa: F401
     control, load, options,
     radamw_decide, radamw_fused_step_multi, radamw_fused_workspace_bytes, radamw_grad_stats,
     radamw_grad_stats_rows, radamw_host_coefficients, radamw_last_hip_error, radamw_launch_count,
-    radamw_list_create, radamw_list_destroy, radamw_list_fused_step, radamw_list_step,
+    radamw_list_create, radamw_list_destroy, radamw_list_fused_step, radamw_list_step, radamw_lists_fused_step,
     radamw_merge_stats, radamw_options_default, radamw_read_report, radamw_stats_plan,
     radamw_status_string, radamw_step, radamw_step_inplace, radamw_step_multi, radamw_step_multi_writeback,
     radamw_step_staged_inplace,

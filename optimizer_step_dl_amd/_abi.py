@@ -157,6 +157,8 @@ def load(path: str = LIB_PATH):
         "radamw_list_step": ([vp, P(u64), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
         "radamw_list_fused_step": ([vp, P(u64), P(Options), dbl, dbl, i32, vp, P(FusedResult)], ctypes.c_int),
         "radamw_list_destroy": ([vp], ctypes.c_int),
+        "radamw_lists_fused_step": ([P(vp), i32, P(u64), P(Options), dbl, dbl, i32, vp, P(FusedResult)],
+                                    ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -172,7 +174,8 @@ EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "rada
            "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
            "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update",
-           "radamw_list_create", "radamw_list_step", "radamw_list_fused_step", "radamw_list_destroy")
+           "radamw_list_create", "radamw_list_step", "radamw_list_fused_step", "radamw_list_destroy",
+           "radamw_lists_fused_step")
 
 
 # ----------------------------------------------------------------- helpers --
@@ -596,6 +599,27 @@ def radamw_list_fused_step(lst: TensorList, step: int, opts: Options, gradient_s
 
 def radamw_list_destroy(lst: TensorList) -> None:
     lst.close()
+
+
+def radamw_lists_fused_step(lists: Sequence[TensorList], steps: Sequence[int], opts: Sequence[Options],
+                            gradient_scale: float, max_grad_norm: Optional[float], hierarchical: bool):
+    """One fused step over several lists (parameter groups): one statistics
+    reduction and one decision, then each list's update with its own options
+    and step count.  Returns (FusedResult, new_steps)."""
+    k = len(lists)
+    if len(steps) != k or len(opts) != k or k == 0:
+        raise ValueError("one step count and one options struct per list")
+    dev = lists[0].device
+    handles = (ctypes.c_void_p * k)(*[lst._live().value for lst in lists])
+    st = (ctypes.c_uint64 * k)(*[int(x) for x in steps])
+    op = (Options * k)(*opts)
+    res = FusedResult()
+    with torch.cuda.device(dev):
+        rc = load().radamw_lists_fused_step(handles, k, st, op, float(gradient_scale),
+                                            0.0 if max_grad_norm is None else float(max_grad_norm),
+                                            int(bool(hierarchical)), _stream(dev), ctypes.byref(res))
+    _check(rc, "radamw_lists_fused_step")
+    return res, [int(x) for x in st]
 
 
 def radamw_host_coefficients(opts: Options, t: int, gradient_scale: float = 1.0) -> list[float]:

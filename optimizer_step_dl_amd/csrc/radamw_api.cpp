@@ -62,6 +62,9 @@ struct DeviceCache {
     std::mutex report_mu;
     radamw_stats *mapped_report_host = nullptr;
     radamw_stats *mapped_report_dev = nullptr;
+    // one merged record per list of a multi-list fused step (report_mu)
+    StatsRec *group_rec = nullptr;
+    int64_t group_cap = 0;
 };
 
 DeviceCache g_devices[MAX_DEVICES];
@@ -456,10 +459,8 @@ void split_launches(const std::vector<SegDesc> &active, std::vector<SegDesc> &so
 // Measurement events, if requested, go on the first and the last launch.
 int submit_updates(const std::vector<SegDesc> &solo, std::vector<SegDesc> &shared, const UpdateTable *resident,
                    const char *resident_base, int gdt, bool ams, bool first, const Coefs &c, int dev,
-                   hipStream_t stream) {
+                   hipStream_t stream, UpdateTiming timing) {
     const size_t launches = solo.size() + (shared.empty() ? 0 : 1);
-    const UpdateTiming timing = g_timing;
-    g_timing = UpdateTiming{};
     size_t k = 0;
     auto ev_start = [&]() { return k == 0 ? timing.start : nullptr; };
     auto ev_stop = [&]() { return k + 1 == launches ? timing.stop : nullptr; };
@@ -492,7 +493,10 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
     const Coefs c = make_coefs(o, *step + 1, gradient_scale);
     std::vector<SegDesc> solo, shared;
     split_launches(active, solo, shared);
-    const int rc = submit_updates(solo, shared, nullptr, nullptr, gdt, o.amsgrad != 0, *step == 0, c, dev, stream);
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    const int rc =
+        submit_updates(solo, shared, nullptr, nullptr, gdt, o.amsgrad != 0, *step == 0, c, dev, stream, timing);
     if (rc != RADAMW_OK) return rc;
     *step += 1;
     *updated = 1;
@@ -644,32 +648,42 @@ std::vector<char> build_stats_table(const std::vector<StatsSeg> &st, int64_t nro
     return bytes;
 }
 
-// Merge the rows and read the 12-byte report back: the final merge writes
-// straight into host memory mapped for the device, so the stream
-// synchronisation is the read-back.
-int report_to_host(const StatsRec *rows, int64_t nrows, StatsRec *scratch, bool hierarchical, int dev,
-                   hipStream_t stream, radamw_stats *host) {
-    DeviceCache &dc = g_devices[dev];
-    std::lock_guard<std::mutex> lock(dc.report_mu);
-    if (!dc.mapped_report_host) {
-        void *hp = nullptr, *dp = nullptr;
-        hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
-        if (e != hipSuccess) return hip_status(e);
-        e = hipHostGetDevicePointer(&dp, hp, 0);
-        if (e != hipSuccess) {
-            (void)hipHostFree(hp);
-            return hip_status(e);
-        }
-        dc.mapped_report_host = static_cast<radamw_stats *>(hp);
-        dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
+// Host memory mapped for the device that receives the final merge, so the
+// stream synchronisation after it is the whole read-back (report_mu held).
+int ensure_mapped(DeviceCache &dc) {
+    if (dc.mapped_report_host) return RADAMW_OK;
+    void *hp = nullptr, *dp = nullptr;
+    hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return hip_status(e);
+    e = hipHostGetDevicePointer(&dp, hp, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(hp);
+        return hip_status(e);
     }
-    StatsRec *mapped = reinterpret_cast<StatsRec *>(dc.mapped_report_dev);
-    int rc = merge_launch(rows, nrows, scratch, mapped, hierarchical, stream);
-    if (rc) return rc;
+    dc.mapped_report_host = static_cast<radamw_stats *>(hp);
+    dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
+    return RADAMW_OK;
+}
+
+// Synchronise the stream and copy the mapped report out (report_mu held).
+int read_mapped(DeviceCache &dc, hipStream_t stream, radamw_stats *host) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_status(e);
     std::memcpy(host, dc.mapped_report_host, sizeof *host);
     return RADAMW_OK;
+}
+
+// Merge the rows and read the 12-byte report back.
+int report_to_host(const StatsRec *rows, int64_t nrows, StatsRec *scratch, bool hierarchical, int dev,
+                   hipStream_t stream, radamw_stats *host) {
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.report_mu);
+    int rc = ensure_mapped(dc);
+    if (rc) return rc;
+    if ((rc = merge_launch(rows, nrows, scratch, reinterpret_cast<StatsRec *>(dc.mapped_report_dev), hierarchical,
+                           stream)))
+        return rc;
+    return read_mapped(dc, stream, host);
 }
 
 }  // namespace
@@ -692,6 +706,7 @@ struct radamw_list_s {
     int64_t nrows = 0;
     size_t stats_coarse_off = 0;
     char *mem = nullptr;      // device: [update table][stats table][rows][merge scratch]
+    char *staging = nullptr;  // pinned host copy of the tables, the source of their upload
     size_t table_off = 0, stats_off = 0, rows_off = 0;
     hipEvent_t done = nullptr;  // recorded after the last launch that reads `mem`
     bool pending = false;
@@ -729,16 +744,41 @@ int list_step_checks(radamw_list_s *l, const radamw_options *opts, const uint64_
 
 // The update launches of one list step, then the event that guards `mem`.
 int list_update(radamw_list_s *l, uint64_t *step, const radamw_options &o, double gradient_scale,
-                hipStream_t stream) {
+                hipStream_t stream, UpdateTiming timing) {
     const Coefs c = make_coefs(o, *step + 1, gradient_scale);
     int rc = submit_updates(l->solo, l->shared, l->shared.size() > 1 ? &l->table : nullptr, l->mem + l->table_off,
-                            l->gdt, l->amsgrad, *step == 0, c, l->dev, stream);
+                            l->gdt, l->amsgrad, *step == 0, c, l->dev, stream, timing);
     if (rc) return rc;
     hipError_t e = hipEventRecord(l->done, stream);
     if (e != hipSuccess) return hip_status(e);
     l->pending = true;
     *step += 1;
     return RADAMW_OK;
+}
+
+StatsRec *list_rows(radamw_list_s *l) { return reinterpret_cast<StatsRec *>(l->mem + l->rows_off); }
+
+// Order a step after the list's previous work (the table upload, the last
+// update), which may have gone to another stream.
+int list_wait(radamw_list_s *l, hipStream_t stream) {
+    if (!l->pending) return RADAMW_OK;
+    return hip_status(hipStreamWaitEvent(stream, l->done, 0));
+}
+
+// The analysis launch of a list (its rows go to the list's own memory).
+int list_analyze(radamw_list_s *l, hipStream_t stream) {
+    int rc;
+    if (l->st.size() == 1) {
+        const StatsSeg &g = l->st[0];
+        rc = hip_status(launch_analyze(g.g, l->gdt, g.n, g.head, g.rows, list_rows(l), stream));
+    } else {
+        const char *base = l->mem + l->stats_off;
+        rc = hip_status(launch_analyze_table(reinterpret_cast<const StatsSeg *>(base),
+                                             reinterpret_cast<const int32_t *>(base + l->stats_coarse_off),
+                                             l->nrows, l->gdt, list_rows(l), stream));
+    }
+    if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
+    return rc;
 }
 
 }  // namespace
@@ -1170,15 +1210,11 @@ int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gd
     l->rows_off = align_up(l->stats_off + stats_table.size(), 256);
     const size_t total = l->rows_off + static_cast<size_t>(l->nrows) * 12 + static_cast<size_t>(se) * 4;
     DeviceScope scope(dev);
-    if (total > 0) {
-        hipError_t e = hipMalloc(&l->mem, total);
-        if (e != hipSuccess) {
-            l->mem = nullptr;
-            return hip_status(e);
-        }
-    }
+    bool copying = false;
     auto fail = [&](hipError_t e) {
-        (void)hipFree(l->mem);
+        if (copying) (void)hipStreamSynchronize(stream);
+        if (l->mem) (void)hipFree(l->mem);
+        if (l->staging) (void)hipHostFree(l->staging);
         if (l->done) (void)hipEventDestroy(l->done);
         return hip_status(e);
     };
@@ -1187,15 +1223,26 @@ int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gd
         l->done = nullptr;
         return fail(e);
     }
-    if (!l->table.bytes.empty() &&
-        (e = hipMemcpyAsync(l->mem + l->table_off, l->table.bytes.data(), l->table.bytes.size(),
-                            hipMemcpyHostToDevice, stream)) != hipSuccess)
+    if (total > 0 && (e = hipMalloc(&l->mem, total)) != hipSuccess) {
+        l->mem = nullptr;
         return fail(e);
-    if (!stats_table.empty() &&
-        (e = hipMemcpyAsync(l->mem + l->stats_off, stats_table.data(), stats_table.size(), hipMemcpyHostToDevice,
-                            stream)) != hipSuccess)
-        return fail(e);
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return fail(e);
+    }
+    // the tables go up from pinned memory the list keeps, so creation does
+    // not wait for the stream; the event guards both buffers
+    const size_t table_bytes = l->stats_off + stats_table.size();
+    if (table_bytes > 0) {
+        if ((e = hipHostMalloc(&l->staging, table_bytes, hipHostMallocDefault)) != hipSuccess) {
+            l->staging = nullptr;
+            return fail(e);
+        }
+        std::memcpy(l->staging + l->table_off, l->table.bytes.data(), l->table.bytes.size());
+        std::memcpy(l->staging + l->stats_off, stats_table.data(), stats_table.size());
+        copying = true;
+        if ((e = hipMemcpyAsync(l->mem, l->staging, table_bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+            return fail(e);
+        if ((e = hipEventRecord(l->done, stream)) != hipSuccess) return fail(e);
+        l->pending = true;
+    }
     *list_out = l.release();
     return RADAMW_OK;
 }
@@ -1212,7 +1259,10 @@ int radamw_list_step(radamw_list list, uint64_t *step, const radamw_options *opt
         *updated = 0;
         return RADAMW_OK;
     }
-    if ((rc = list_update(list, step, *opts, ctrl->gradient_scale, stream))) return rc;
+    if ((rc = list_wait(list, stream))) return rc;
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    if ((rc = list_update(list, step, *opts, ctrl->gradient_scale, stream, timing))) return rc;
     *updated = 1;
     return RADAMW_OK;
 }
@@ -1230,19 +1280,10 @@ int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_option
     std::memset(result, 0, sizeof *result);
     result->clip_coef = 1.0;
     if (list->active == 0) return RADAMW_OK;
-    StatsRec *rows = reinterpret_cast<StatsRec *>(list->mem + list->rows_off);
-    if (list->st.size() == 1) {
-        const StatsSeg &g = list->st[0];
-        rc = hip_status(launch_analyze(g.g, list->gdt, g.n, g.head, g.rows, rows, stream));
-    } else {
-        const char *base = list->mem + list->stats_off;
-        rc = hip_status(launch_analyze_table(reinterpret_cast<const StatsSeg *>(base),
-                                             reinterpret_cast<const int32_t *>(base + list->stats_coarse_off),
-                                             list->nrows, list->gdt, rows, stream));
-    }
-    if (rc) return rc;
-    g_launches.fetch_add(1, std::memory_order_relaxed);
+    if ((rc = list_wait(list, stream))) return rc;
+    if ((rc = list_analyze(list, stream))) return rc;
     radamw_stats host;
+    StatsRec *rows = list_rows(list);
     if ((rc = report_to_host(rows, list->nrows, rows + list->nrows, hierarchical != 0, list->dev, stream, &host)))
         return rc;
     radamw_control ctrl;
@@ -1251,7 +1292,94 @@ int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_option
         result->updated = 0;
         return RADAMW_OK;
     }
-    if ((rc = list_update(list, step, *opts, ctrl.gradient_scale, stream))) return rc;
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    if ((rc = list_update(list, step, *opts, ctrl.gradient_scale, stream, timing))) return rc;
+    result->updated = 1;
+    return RADAMW_OK;
+}
+
+int radamw_lists_fused_step(const radamw_list *lists, int32_t nlists, uint64_t *steps,
+                            const radamw_options *opts, double gradient_scale, double max_grad_norm,
+                            int32_t hierarchical, radamw_stream_t stream_, radamw_fused_result *result) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if (!lists || !steps || !opts || !result || nlists < 1 || nlists > 65536) return RADAMW_ERR_INVALID;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    if (!is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    if (hierarchical != 0 && hierarchical != 1) return RADAMW_ERR_INVALID;
+    std::vector<radamw_list_s *> sorted(lists, lists + nlists);
+    for (radamw_list_s *l : sorted)
+        if (!l) return RADAMW_ERR_INVALID;
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return RADAMW_ERR_INVALID;
+    for (int32_t k = 0; k < nlists; ++k)
+        if ((rc = list_step_checks(lists[k], &opts[k], &steps[k], stream))) return rc;
+    // every list locked for the whole step, in address order
+    std::vector<std::unique_lock<std::mutex>> locks;
+    locks.reserve(sorted.size());
+    for (radamw_list_s *l : sorted) locks.emplace_back(l->mu);
+    std::memset(result, 0, sizeof *result);
+    result->clip_coef = 1.0;
+    std::vector<int32_t> act;  // lists with at least one non-empty tensor, in call order
+    for (int32_t k = 0; k < nlists; ++k)
+        if (lists[k]->active > 0) act.push_back(k);
+    if (act.empty()) return RADAMW_OK;
+    const int dev = lists[act[0]]->dev;
+    for (int32_t k : act)
+        if ((rc = list_wait(lists[k], stream))) return rc;
+    for (int32_t k : act)
+        if ((rc = list_analyze(lists[k], stream))) return rc;
+    radamw_stats host;
+    if (act.size() == 1) {
+        radamw_list_s *l = lists[act[0]];
+        StatsRec *rows = list_rows(l);
+        if ((rc = report_to_host(rows, l->nrows, rows + l->nrows, hierarchical != 0, dev, stream, &host))) return rc;
+    } else {
+        // each list's rows reduce to one record; the records, in call
+        // order, take one final merge into the mapped report
+        DeviceCache &dc = g_devices[dev];
+        std::lock_guard<std::mutex> lock(dc.report_mu);
+        if ((rc = ensure_mapped(dc))) return rc;
+        const int64_t nact = static_cast<int64_t>(act.size());
+        if (dc.group_cap < nact) {
+            DeviceScope scope(dev);
+            if (dc.group_rec) (void)hipFree(dc.group_rec);
+            dc.group_rec = nullptr;
+            dc.group_cap = 0;
+            const int64_t cap = std::max<int64_t>(nact, 256);
+            hipError_t e = hipMalloc(&dc.group_rec, static_cast<size_t>(cap) * sizeof(StatsRec));
+            if (e != hipSuccess) {
+                dc.group_rec = nullptr;
+                return hip_status(e);
+            }
+            dc.group_cap = cap;
+        }
+        for (int64_t i = 0; i < nact; ++i) {
+            radamw_list_s *l = lists[act[i]];
+            StatsRec *rows = list_rows(l);
+            if ((rc = merge_launch(rows, l->nrows, rows + l->nrows, dc.group_rec + i, hierarchical != 0, stream)))
+                return rc;
+        }
+        rc = hip_status(launch_merge(dc.group_rec, nact, nact, 1, reinterpret_cast<StatsRec *>(dc.mapped_report_dev),
+                                     stream));
+        if (rc) return rc;
+        g_launches.fetch_add(1, std::memory_order_relaxed);
+        if ((rc = read_mapped(dc, stream, &host))) return rc;
+    }
+    radamw_control ctrl;
+    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
+    if (ctrl.skip_update) {
+        result->updated = 0;
+        return RADAMW_OK;
+    }
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    for (size_t i = 0; i < act.size(); ++i) {
+        const int32_t k = act[i];
+        const UpdateTiming t{i == 0 ? timing.start : nullptr, i + 1 == act.size() ? timing.stop : nullptr};
+        if ((rc = list_update(lists[k], &steps[k], opts[k], ctrl.gradient_scale, stream, t))) return rc;
+    }
     result->updated = 1;
     return RADAMW_OK;
 }
@@ -1267,6 +1395,7 @@ int radamw_list_destroy(radamw_list list) {
             if (e != hipSuccess) rc = hip_status(e);
         }
         if (list->mem) (void)hipFree(list->mem);
+        if (list->staging) (void)hipHostFree(list->staging);
         if (list->done) (void)hipEventDestroy(list->done);
     }
     delete list;

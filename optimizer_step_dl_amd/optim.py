@@ -23,9 +23,15 @@ Behaviour (TR-zh):
     with the fused and hierarchical modes off.
 
 All arithmetic runs in the library's kernels; this class only groups
-tensors (by parameter group and by step count, since one launch shares one
-step count) and sequences the C entry points.  Parameters must be FP32
-device tensors; gradients FP32, FP16 or BF16 of the same shape.
+tensors into launch buckets (parameter group, gradient dtype, model-copy
+dtype, step count: one launch shares one options struct, one dtype and one
+step count) and calls the C entry points.  Each bucket is a persistent
+tensor list, validated once and reused while its tensors keep their
+storage, and a fused step is one radamw_lists_fused_step call over all of
+them.  A cached list holds references to the tensors it was built from
+(including the gradients of the last step) until it is rebuilt or freed.
+Parameters must be FP32 device tensors; gradients FP32, FP16 or BF16 of the
+same shape.
 """
 from __future__ import annotations
 
@@ -55,7 +61,7 @@ class FusedAdamW(torch.optim.Optimizer):
         self.fused_step = bool(fused_step)
         self.max_grad_norm = max_grad_norm
         self.hierarchical_stats = bool(hierarchical_stats)
-        self._workspace: Optional[torch.Tensor] = None
+        self._cache: dict = {}  # bucket -> (storage signature, TensorList)
         self.last_result: Optional[_abi.FusedResult] = None
         self._copies: dict = {}
         for master, copy in (model_copies or {}).items():
@@ -109,6 +115,47 @@ class FusedAdamW(torch.optim.Optimizer):
         return _abi.Segment(p, p.grad, st["exp_avg"], st["exp_avg_sq"], st.get("max_exp_avg_sq"))
 
     # ------------------------------------------------------------- step --
+    def _lists(self, active):
+        """Launch buckets -- (parameter group, gradient dtype, model-copy
+        dtype, step count), since one launch shares one options struct, one
+        gradient dtype and one step count -- each as a persistent tensor list
+        [(TensorList, group, members)].  A cached list is reused while its
+        tensors keep their storage; a list whose tensors moved (a new
+        ``.grad`` tensor, a loaded state) is rebuilt, and lists no bucket
+        uses any more are freed."""
+        buckets = {}
+        for group, items in active:
+            for p, st in items:
+                copy = self._copies.get(p)
+                key = (id(group), bool(group["amsgrad"]), p.grad.dtype, None if copy is None else copy.dtype,
+                       st["step"])
+                buckets.setdefault(key, (group, []))[1].append((p, st))
+        out, used = [], set()
+        for key, (group, members) in buckets.items():
+            ident = key[:4] + (tuple(id(p) for p, _ in members),)
+            sig = tuple((p.data_ptr(), p.grad.data_ptr(), st["exp_avg"].data_ptr(), st["exp_avg_sq"].data_ptr(),
+                         st["max_exp_avg_sq"].data_ptr() if "max_exp_avg_sq" in st else 0,
+                         self._copies[p].data_ptr() if p in self._copies else 0, p.numel())
+                        for p, st in members)
+            cached = self._cache.get(ident)
+            if cached is None or cached[0] != sig:
+                if cached is not None:
+                    cached[1].close()
+                segs = [self._segment(p, st) for p, st in members]
+                copies = None if key[3] is None else [self._copies[p] for p, _ in members]
+                cached = (sig, _abi.TensorList(segs, group["amsgrad"], copies))
+                self._cache[ident] = cached
+            used.add(ident)
+            out.append((cached[1], group, members))
+        for ident in [k for k in self._cache if k not in used]:
+            self._cache.pop(ident)[1].close()
+        return out
+
+    def _release_lists(self):
+        for _, lst in self._cache.values():
+            lst.close()
+        self._cache.clear()
+
     @torch.no_grad()
     def step(self, closure=None, gradient_scale: float = 1.0):
         """One update of every parameter with a gradient.  ``gradient_scale``
@@ -119,54 +166,26 @@ class FusedAdamW(torch.optim.Optimizer):
             with torch.enable_grad():
                 loss = closure()
         active = self._active()
+        self.last_result = None
         if not active:
             return loss
-        ctrl = _abi.control(gradient_scale, False)
-        self.last_result = None
+        lists = self._lists(active)
         if self.fused_step:
-            ctrl = self._fused_decision(active, gradient_scale)
-            if ctrl is None:
-                return loss  # whole step skipped: non-finite gradient
-        for group, items in active:
-            opts = self._options(group)
-            by_step = {}  # one launch set per (step count, model-copy dtype)
-            for p, st in items:
-                copy = self._copies.get(p)
-                key = (st["step"], None if copy is None else copy.dtype)
-                by_step.setdefault(key, []).append((p, st))
-            for (step, copy_dtype), members in by_step.items():
-                segs = [self._segment(p, st) for p, st in members]
-                if copy_dtype is None:
-                    _, new_step = _abi.radamw_step_multi(segs, step, opts, ctrl)
-                else:
-                    copies = [self._copies[p] for p, _ in members]
-                    _, new_step = _abi.radamw_step_multi_writeback(segs, copies, step, opts, ctrl)
-                for _, st in members:
-                    st["step"] = new_step
+            # statistics of every active gradient -> one 12-byte report ->
+            # one decision for all buckets -> each bucket's update
+            res, steps = _abi.radamw_lists_fused_step(
+                [lst for lst, _, _ in lists], [members[0][1]["step"] for _, _, members in lists],
+                [self._options(group) for _, group, _ in lists], gradient_scale, self.max_grad_norm,
+                self.hierarchical_stats)
+            self.last_result = res
+        else:
+            ctrl = _abi.control(gradient_scale, False)
+            steps = [lst.step(members[0][1]["step"], self._options(group), ctrl)[1]
+                     for lst, group, members in lists]
+        for (_, _, members), new_step in zip(lists, steps):
+            for _, st in members:
+                st["step"] = new_step
         return loss
-
-    def _fused_decision(self, active, gradient_scale: float):
-        """Statistics of every active gradient -> merge -> 12-byte read-back ->
-        decision.  Returns the control for the update, or None to skip."""
-        grads = [p.grad for _, items in active for p, _ in items]
-        dev = grads[0].device
-        rows_total = sum(_abi.radamw_grad_stats_rows(g.numel(), g.dtype) for g in grads)
-        scratch_elems = _abi.radamw_stats_plan(rows_total)[0] if rows_total else 0
-        words = 3 * rows_total + scratch_elems + 3
-        if self._workspace is None or self._workspace.numel() < words or self._workspace.device != dev:
-            self._workspace = torch.empty(words, dtype=torch.int32, device=dev)
-        ws = self._workspace
-        rows = ws[:3 * rows_total]
-        off = 0
-        for g in grads:
-            off += _abi.radamw_grad_stats(g.contiguous() if not g.is_contiguous() else g, rows, off)
-        scratch = ws[3 * rows_total:3 * rows_total + scratch_elems].view(torch.float32) if scratch_elems else None
-        report = ws[3 * rows_total + scratch_elems:3 * rows_total + scratch_elems + 3]
-        _abi.radamw_merge_stats(rows, rows_total, scratch, report, self.hierarchical_stats)
-        host = _abi.radamw_read_report(report)
-        ctrl, result = _abi.radamw_decide(host, gradient_scale, self.max_grad_norm)
-        self.last_result = result
-        return None if ctrl.skip_update else ctrl
 
     # ------------------------------------------------------- checkpoints --
     def step_options(self) -> dict:
@@ -183,6 +202,7 @@ class FusedAdamW(torch.optim.Optimizer):
         return sd
 
     def load_state_dict(self, state_dict):
+        self._release_lists()
         state_dict = dict(state_dict)
         opts = state_dict.pop("step_options", None)
         super().load_state_dict(state_dict)

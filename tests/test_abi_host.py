@@ -218,3 +218,30 @@ def test_list_entry_points_validate_before_any_device_call(lib):
     assert lib.radamw_list_destroy(None) == 0
     assert step.value == 3 and upd.value == -7
     assert ra.radamw_launch_count() == before
+
+
+def test_lists_fused_step_validates_before_any_device_call(lib):
+    """The multi-list fused step rejects a bad array before it reads any
+    handle: a handle given twice is caught before it is dereferenced."""
+    before = ra.radamw_launch_count()
+    res = _abi.FusedResult()
+    steps = (ctypes.c_uint64 * 2)(4, 4)
+    opts = (_abi.Options * 2)(ra.options(), ra.options())
+    fake = ctypes.c_void_p(0x1000)
+    twice = (ctypes.c_void_p * 2)(fake.value, fake.value)
+    with_null = (ctypes.c_void_p * 2)(fake.value, None)
+    call = lambda lists, n, scale=1.0, clip=1.0, hier=1, st=steps, op=opts, out=res: lib.radamw_lists_fused_step(
+        lists, n, st, op, scale, clip, hier, None, ctypes.byref(out) if out is not None else None)
+    assert call(twice, 2) == -1                   # the same handle twice
+    assert call(with_null, 2) == -1               # a NULL handle
+    assert call(None, 2) == -1
+    assert call(twice, 0) == -1                   # no lists
+    assert call(twice, 65537) == -1               # too many lists
+    assert call(twice, 2, scale=0.0) == -1
+    assert call(twice, 2, clip=float("inf")) == -1
+    assert call(twice, 2, hier=3) == -1
+    assert call(twice, 2, st=None) == -1
+    assert call(twice, 2, op=None) == -1
+    assert call(twice, 2, out=None) == -1
+    assert list(steps) == [4, 4]
+    assert ra.radamw_launch_count() == before

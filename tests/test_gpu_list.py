@@ -218,3 +218,79 @@ def test_list_fused_launch_count_and_reuse():
             assert ra.radamw_launch_count() - before == 1 + extra + 1 + 2  # stats, merges, solo + shared
     torch.cuda.synchronize()
     assert all(torch.isfinite(s.param).all() for s in segs)
+
+
+def test_lists_fused_step_two_groups_match_oracle():
+    """Two parameter groups (AMSGrad with strong decay; AdamW) at different
+    step counts: one statistics reduction over both, one clip decision, each
+    group updated with its own options; an injected NaN skips both."""
+    announce("lists fused step, two groups")
+    gdt, key, max_norm, scale = "f16", (0, "lists2"), 0.05, 1024.0
+    sizes_a, sizes_b = [4096, 2049, SOLO + 3], [1, 70_001, 0, 3000]
+    opts_a = ra.options(lr=1e-2, weight_decay=0.1, amsgrad=True)
+    opts_b = ra.options(lr=1e-3, weight_decay=0.01)
+    segs_a, refs_a = _make(sizes_a, gdt, True, key + ("a",), misaligned=False)
+    segs_b, refs_b = _make(sizes_b, gdt, False, key + ("b",), misaligned=False)
+    groups = [(segs_a, refs_a, sizes_a, opts_a), (segs_b, refs_b, sizes_b, opts_b)]
+    # group b starts three updates behind group a's count
+    steps = [3, 0]
+    for r in refs_a:
+        r[1].step = 3
+    for s in segs_a:  # a steady state for the AMSGrad group, mirrored into the oracle
+        s.exp_avg.fill_(1e-5); s.exp_avg_sq.fill_(1e-8); s.max_exp_avg_sq.fill_(2e-8)
+    for r in refs_a:
+        r[1].exp_avg[:] = np.float32(1e-5); r[1].exp_avg_sq[:] = np.float32(1e-8)
+        r[1].max_exp_avg_sq[:] = np.float32(2e-8)
+    with ra.TensorList(segs_a, True) as la, ra.TensorList(segs_b, False) as lb:
+        for t in range(1, 4):
+            grads = []
+            for gi, (segs, _, sizes, _) in enumerate(groups):
+                for i, s in enumerate(segs):
+                    s.grad.copy_(synth.stored_grad(sizes[i], 1e-4, scale, gdt, key + (gi, i, "g", t)).to(DEV))
+                    grads.append(s.grad)
+            if t == 2:
+                segs_b[1].grad[777] = float("nan")
+            acc = oracle.StatsAccumulator()
+            for g in grads:
+                acc.add(grad_host(g), gdt)
+            sumsq, count = acc.result
+            skip, eff = oracle.decide(sumsq, count, scale, max_norm)
+            res, new_steps = ra.radamw_lists_fused_step([la, lb], steps, [opts_a, opts_b], scale, max_norm, True)
+            torch.cuda.synchronize()
+            assert bool(res.found_inf) == skip == (t == 2) and res.nonfinite == count
+            assert abs(res.sumsq - sumsq) <= (sum(sizes_a + sizes_b) * 2.0**-53 + 1e-12) * sumsq
+            if skip:
+                assert new_steps == steps and not res.updated
+            else:
+                assert new_steps == [steps[0] + 1, steps[1] + 1] and res.updated and res.clip_coef < 1.0
+            steps = new_steps
+            for segs, refs, sizes, opts in groups:
+                for i, s in enumerate(segs):
+                    if sizes[i] == 0:
+                        continue
+                    oracle.adamw_step(refs[i][0], grad_host(s.grad), gdt, refs[i][1], oracle_opts(opts), eff, skip)
+                    contract_one_step(host(s.param), refs[i][0], f"step {t} n={sizes[i]} p")
+                    contract_one_step(host(s.exp_avg_sq), refs[i][1].exp_avg_sq, f"step {t} n={sizes[i]} v")
+        assert steps == [5, 2]
+
+
+def test_lists_fused_step_of_one_list_is_list_fused_step():
+    announce("lists fused step, one list")
+    gdt, key = "bf16", (0, "lists1")
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    segs, _ = _make(SIZES, gdt, False, key)
+    twins, _ = _make(SIZES, gdt, False, key)
+    with ra.TensorList(segs, False) as la, ra.TensorList(twins, False) as lb:
+        sa = sb = 0
+        for t in range(1, 4):
+            _fill_grads(segs, twins, SIZES, gdt, 1.0, key, t)
+            ra_, (sa,) = ra.radamw_lists_fused_step([la], [sa], [opts], 1.0, 0.05, True)
+            rb, sb = lb.fused_step(sb, opts, 1.0, 0.05, True)
+            torch.cuda.synchronize()
+            assert (ra_.sumsq, ra_.nonfinite, ra_.clip_coef, ra_.updated) == (rb.sumsq, rb.nonfinite, rb.clip_coef,
+                                                                               rb.updated)
+            assert sa == sb == t
+            for i, (s, tw) in enumerate(zip(segs, twins)):
+                _same_bits(s, tw, False, f"step {t} segment {i}")
+        with pytest.raises(ra.RadamwError):  # the same list twice
+            ra.radamw_lists_fused_step([la, la], [sa, sa], [opts, opts], 1.0, 1.0, True)

@@ -158,3 +158,30 @@ def test_close_to_torch_adamw_on_gpu():
     for a, b in zip(pa, pb):
         ref = host(b).astype(np.float64)
         assert np.abs(host(a) - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_bucket_lists_reused_while_storage_unchanged():
+    """Each launch bucket is a persistent tensor list: gradients refreshed
+    in place keep the lists; new gradient tensors rebuild them; a group whose
+    tensors have no gradient frees its list."""
+    announce("FusedAdamW list cache")
+    key = (0, "optc")
+    params = _model(key)
+    opt = FusedAdamW(_groups(params), fused_step=True, max_grad_norm=1.0)
+    _set_grads(params, 1, key)
+    opt.step()
+    first = {k: v[1] for k, v in opt._cache.items()}
+    assert len(first) == 2  # one list per parameter group
+    for i, p in enumerate(params):
+        p.grad.copy_(synth.stored_grad(p.numel(), 1e-3, 1.0, "f32", key + (i, "g", 2)).to(DEV))
+    opt.step()
+    assert {k: v[1] for k, v in opt._cache.items()} == first
+    _set_grads(params, 3, key)
+    opt.step()
+    third = {k: v[1] for k, v in opt._cache.items()}
+    assert len(third) == 2 and all(third[k] is not first[k] for k in third)
+    _set_grads(params, 4, key, which={0, 1})  # the second group has no gradient
+    opt.step()
+    assert len(opt._cache) == 1
+    torch.cuda.synchronize()
+    assert [opt.state[p]["step"] for p in params] == [4, 4, 3, 3]

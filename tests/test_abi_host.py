@@ -245,3 +245,25 @@ def test_lists_fused_step_validates_before_any_device_call(lib):
     assert call(twice, 2, out=None) == -1
     assert list(steps) == [4, 4]
     assert ra.radamw_launch_count() == before
+
+
+@pytest.mark.parametrize("betas", [(0.9, 0.999), (0.95, 0.9999)])
+def test_host_coefficients_at_late_steps(lib, betas):
+    """t in [1e4, 1e6]: the library's lr/bc1 and 1/bc2 stay within one FP32
+    ulp of the correctly rounded exact values (80-digit decimal powers),
+    and its betas are the oracle's."""
+    import decimal
+    opts = ra.options(lr=1e-3, beta1=betas[0], beta2=betas[1], weight_decay=0.01)
+    oopts = oracle.Options(lr=1e-3, beta1=betas[0], beta2=betas[1], weight_decay=0.01)
+    for t in sorted(set(int(round(x)) for x in np.logspace(4, 6, 21))):
+        c = ra.radamw_host_coefficients(opts, t, 1.0)
+        o = oracle.coefficients(oopts, t)
+        assert np.float32(c[0]) == o["beta1"] and np.float32(c[2]) == o["beta2"]
+        with decimal.localcontext() as ctx:
+            ctx.prec = 80
+            bc1 = 1 - decimal.Decimal(betas[0]) ** t
+            bc2 = 1 - decimal.Decimal(betas[1]) ** t
+            step = np.float32(float(decimal.Decimal(1e-3) / bc1))
+            ibc2 = np.float32(float(1 / bc2))
+        for got, want in ((np.float32(c[6]), step), (np.float32(c[7]), ibc2)):
+            assert abs(int(got.view(np.int32)) - int(want.view(np.int32))) <= 1, (t, got, want)

@@ -347,6 +347,32 @@ def test_bias_corrections_match_exact_arithmetic(betas):
     assert c["decay"] == np.float32(1 - Fraction(1e-3) * Fraction(1e-4))
 
 
+def _decimal_bias(beta: float, t: int) -> np.float32:
+    """FP32 rounding of 1 - beta^t with beta^t evaluated in 80-digit decimal
+    arithmetic from the exact binary value of beta."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 80
+        val = 1 - decimal.Decimal(beta) ** t
+        return np.float32(float(val))
+
+
+@pytest.mark.parametrize("betas", [(0.9, 0.999), (0.8, 0.95), (0.95, 0.9999)])
+def test_bias_corrections_up_to_a_million_steps(betas):
+    """Late steps (t in [1e4, 1e6], log-spaced, plus the region where
+    1 - beta2^t reaches 1 in FP32): the oracle's FP64 power stays within the
+    correctly rounded FP32 value of the exact quantity."""
+    opts = oracle.Options(beta1=betas[0], beta2=betas[1])
+    ts = sorted(set(int(round(x)) for x in np.logspace(4, 6, 25)) | {16_000, 17_000, 18_000, 170_000, 180_000})
+    for t in ts:
+        c = oracle.coefficients(opts, t)
+        for beta, key in ((betas[0], "bc1"), (betas[1], "bc2")):
+            want = _decimal_bias(beta, t)
+            assert c[key] == want, (t, key, c[key], want)
+    # beyond the point where beta2^t < 2^-25 the FP32 bias correction is exactly 1
+    assert oracle.coefficients(oracle.Options(), 1_000_000)["bc2"] == np.float32(1.0)
+
+
 # --------------------------------------------------------------- decoding --
 
 def test_half_decoder_matches_numpy_for_all_bit_patterns():

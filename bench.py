@@ -6,16 +6,17 @@
 One timed step is one pass of the whole path over a 268,435,456-element flat
 FP32 bucket (FP32 gradients, steady state at t = 1000, moments pre-warmed),
 one radamw_fused_step_multi call: gradient statistics, the hierarchical
-fan-in-1024 merge, the 12-byte report read back to the host (the step's one
-synchronisation), the skip / clip decision (global norm clipped at 1.0), and
-the in-place fused update.  Inputs are resident in HBM before the timer
-starts.  Inside the timed region the update kernel's own start / end HIP
+fan-in-1024 merge whose final kernel also takes the skip / clip decision
+(global norm clipped at 1.0) on the device, the in-place fused update queued
+right behind it, and the 12-byte report read back to the host (the step's
+one wait, which overlaps the update).  Inputs are resident in HBM before the
+timer starts.  Inside the timed region the update kernel's own start / end HIP
 events (radamw_time_next_update: hipExtLaunchKernelGGL on the launch stream)
 give the kernel duration the roofline object uses.
 
 Prints ONE JSON line (rank 0).  Extra keys beside the contract's:
-"roofline", "cpu_baseline", "kernels" (update kernel timing, rest of the
-step), "variants" (update-only timings of the bucket's other
+"roofline", "cpu_baseline", "cpu_baseline_all_cores", "kernels" (update
+kernel timing, rest of the step), "device" (GPU, versions, clocks), "variants" (update-only timings of the bucket's other
 configurations), "staged_vs_fused" (the pages' staged baseline A/B),
 "decoder_1b_list" (per-tensor vs radamw_step_multi launches),
 "decoder_7b_fused_step" (the whole step over a 6.7B-parameter list),
@@ -175,7 +176,7 @@ def main(argv=None):
         "update_adamw_f32_inplace": {"avg_ms": upd_avg, "min_ms": min(upd_ms), "max_ms": max(upd_ms),
                                      "bytes_per_param": bpp, "gbs": achieved},
         "rest_of_step": {"avg_ms": ms_per_step - upd_avg, "what": "grad statistics (4 B/param read), "
-                         f"{ex} merge level(s) + final merge, 12-byte read-back, decision, launch latencies",
+                         f"{ex} merge level(s) + final merge, decision taken on the device by the final merge (the host reads the 12-byte report while the update runs), launch latencies",
                          "rows": rows_n, "extra_merge_kernels": ex},
     }
     del p, g, m, v, ws, seglist

@@ -293,8 +293,8 @@ int radamw_merge_stats(const radamw_stats *rows, int64_t nrows, float *scratch,
 
 /*
  * Read a device report back to the host (hipMemcpyAsync through a pinned
- * staging buffer, then stream synchronisation).  This is the one place the
- * step waits for the device (TR-zh: the report is read back before any
+ * staging buffer, then stream synchronisation): the read-back of the step
+ * composed from separate calls (TR-zh: the report is read back before any
  * update).  host_report: host struct.
  */
 int radamw_read_report(const radamw_stats *report, radamw_stats *host_report,
@@ -317,15 +317,24 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale,
  * The whole fused step over a tensor list, the ruda_torch.AdamW
  * fused_step path of TR-zh: statistics of every active gradient ->
  * (hierarchical) merge -> 12-byte report read back -> skip or clip decision
- * -> one in-place radamw_step_multi launch.
+ * -> the in-place update of radamw_step_multi.
  *   workspace : device, >= radamw_fused_workspace_bytes(...) bytes, 4-byte
- *               aligned, caller-owned (rows, merge scratch and a reserved
- *               report slot).  The final merge writes the report directly
- *               into host memory the library maps for the device, so the
- *               read-back is the stream synchronisation alone.
+ *               aligned, caller-owned: the rows, the merge scratch and a
+ *               12-byte decision slot (its last 12 bytes).
  *   max_grad_norm <= 0 disables clipping.
  *   result    : host struct, always filled on RADAMW_OK.
- * Synchronises the stream once (the report read-back).
+ * The final merge writes the report into host memory the library maps for
+ * the device, and takes the same skip / clip decision as radamw_decide on
+ * the device as well (the same binary64 operations, each correctly
+ * rounded), writing it to the decision slot.  The update launches are
+ * queued right behind the merge and read that slot, so the GPU never waits
+ * for the host; the host waits once, for the merge, reads the report, takes
+ * the decision itself and advances *step when the update ran.  When the
+ * report counts a non-finite value the queued update kernels write nothing
+ * (they have already issued their reads, so a skipped step costs one read
+ * pass; skips are rare).  The two decisions always agree; if they did not,
+ * the call would return RADAMW_ERR_HIP.  The workspace stays in use until
+ * the stream has passed the update kernels.
  */
 int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg,
                                      radamw_dtype gdt);
@@ -382,8 +391,8 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
  * radamw_list_fused_step(list, step, opts, gradient_scale, max_grad_norm,
  *                        hierarchical, stream, result)
  *   radamw_fused_step_multi over the list's segments, using the list's own
- *   rows and scratch as the workspace.  Synchronises the stream once (the
- *   report read-back).
+ *   rows, scratch and decision slot as the workspace; the host waits once,
+ *   for the final merge.
  *
  * Calls on one list serialise on a lock inside it, and each step's first
  * kernel waits (hipStreamWaitEvent) for the list's previous work, the table
@@ -427,9 +436,12 @@ int radamw_list_destroy(radamw_list list);
  *   rows are merged to one record (with the fan-in-1024 levels when
  *   hierarchical = 1), and those records, in array order, take one final
  *   merge into the report.  With a single non-empty list this is exactly
- *   radamw_list_fused_step.  The decision is taken once on that report: a
- *   non-finite value anywhere skips every list; otherwise every list
- *   updates with the same clipped scale and its own options and step.
+ *   radamw_list_fused_step.  The decision is taken once on that report
+ *   (on the device by the final merge, into the first non-empty list's
+ *   decision slot, which every list's queued update kernels read; and on
+ *   the host after the one wait): a non-finite value anywhere skips every
+ *   list; otherwise every list updates with the same clipped scale and its
+ *   own options and step.
  *   Lists with no non-empty tensor neither launch nor step.
  *   Errors as radamw_list_fused_step, checked for every list before any
  *   launch; a handle given twice is RADAMW_ERR_INVALID.

@@ -58,16 +58,33 @@ struct DeviceCache {
     // pinned 12-byte staging for report read-back
     radamw_stats *pinned_report = nullptr;
     // host memory mapped for the device: the fused step's final merge writes
-    // its report here directly, so the read-back is only the synchronisation
+    // its report (offset 0) and its decision (offset 16) here directly, so
+    // the read-back is only a wait for the merge (merge_done)
     std::mutex report_mu;
     radamw_stats *mapped_report_host = nullptr;
     radamw_stats *mapped_report_dev = nullptr;
+    Decision *mapped_decision_host = nullptr;
+    Decision *mapped_decision_dev = nullptr;
+    hipEvent_t merge_done = nullptr;
     // one merged record per list of a multi-list fused step (report_mu)
     StatsRec *group_rec = nullptr;
     int64_t group_cap = 0;
 };
 
 DeviceCache g_devices[MAX_DEVICES];
+
+// Temporarily make `dev` the calling thread's current device.
+struct DeviceScope {
+    int prev = -1;
+    explicit DeviceScope(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) (void)hipSetDevice(dev);
+    }
+    ~DeviceScope() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
 
 int stream_device(hipStream_t stream, int *dev) {
     hipDevice_t d = 0;
@@ -290,7 +307,7 @@ int check_update_tensor(const SegDesc &s, int gdt, bool amsgrad, bool first, boo
     return RADAMW_OK;
 }
 
-int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, int dev,
+int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, const Decision *dec, int dev,
                   hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)dev;
     s.head = segment_head(s, gdt, amsgrad, first);
@@ -298,7 +315,7 @@ int launch_single(SegDesc s, int gdt, bool amsgrad, bool first, const Coefs &c, 
     const int64_t tiles = segment_tiles(s.n, s.head);
     if (tiles > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
     const int grid = update_grid(tiles);
-    int rc = hip_status(launch_update_single(s, c, gdt, amsgrad, first, grid, stream, ev_start, ev_stop));
+    int rc = hip_status(launch_update_single(s, c, dec, gdt, amsgrad, first, grid, stream, ev_start, ev_stop));
     if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
     return rc;
 }
@@ -400,24 +417,25 @@ int build_update_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool f
 
 // Launch an update over a table already in device memory at `base`.
 hipError_t launch_table_at(const UpdateTable &t, const char *base, int gdt, bool amsgrad, bool first,
-                           const Coefs &c, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                           const Coefs &c, const Decision *dec, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
     return launch_update_table(reinterpret_cast<const SegDesc *>(base),
                                reinterpret_cast<const int64_t *>(base + t.prefix_off),
-                               reinterpret_cast<const int32_t *>(base + t.coarse_off), t.nseg, t.tiles, c, gdt,
-                               amsgrad, first, update_grid(t.tiles), stream, ev_start, ev_stop);
+                               reinterpret_cast<const int32_t *>(base + t.coarse_off), t.nseg, t.tiles, c, dec,
+                               gdt, amsgrad, first, update_grid(t.tiles), stream, ev_start, ev_stop);
 }
 
 // Several tensors in one launch, the table going through a staged slot
 // (staged_launch).
 int launch_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, const Coefs &c,
-                 int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                 const Decision *dec, int dev, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     UpdateTable t;
     int rc = build_update_table(segs, gdt, amsgrad, first, &t);
     if (rc) return rc;
     return staged_launch(
         dev, stream, t.bytes.size(), [&](char *host) { std::memcpy(host, t.bytes.data(), t.bytes.size()); },
         [&](const char *dev_base) {
-            return launch_table_at(t, dev_base, gdt, amsgrad, first, c, stream, ev_start, ev_stop);
+            return launch_table_at(t, dev_base, gdt, amsgrad, first, c, dec, stream, ev_start, ev_stop);
         });
 }
 
@@ -458,24 +476,25 @@ void split_launches(const std::vector<SegDesc> &active, std::vector<SegDesc> &so
 // resident in device memory (resident != null: its image and device base).
 // Measurement events, if requested, go on the first and the last launch.
 int submit_updates(const std::vector<SegDesc> &solo, std::vector<SegDesc> &shared, const UpdateTable *resident,
-                   const char *resident_base, int gdt, bool ams, bool first, const Coefs &c, int dev,
-                   hipStream_t stream, UpdateTiming timing) {
+                   const char *resident_base, int gdt, bool ams, bool first, const Coefs &c, const Decision *dec,
+                   int dev, hipStream_t stream, UpdateTiming timing) {
     const size_t launches = solo.size() + (shared.empty() ? 0 : 1);
     size_t k = 0;
     auto ev_start = [&]() { return k == 0 ? timing.start : nullptr; };
     auto ev_stop = [&]() { return k + 1 == launches ? timing.stop : nullptr; };
     int rc = RADAMW_OK;
     for (const SegDesc &d : solo) {
-        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream, ev_start(), ev_stop()))) return rc;
+        if ((rc = launch_single(d, gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop()))) return rc;
         ++k;
     }
     if (shared.size() == 1) {
-        rc = launch_single(shared[0], gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+        rc = launch_single(shared[0], gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop());
     } else if (shared.size() > 1 && resident) {
-        rc = hip_status(launch_table_at(*resident, resident_base, gdt, ams, first, c, stream, ev_start(), ev_stop()));
+        rc = hip_status(
+            launch_table_at(*resident, resident_base, gdt, ams, first, c, dec, stream, ev_start(), ev_stop()));
         if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
     } else if (shared.size() > 1) {
-        rc = launch_table(shared, gdt, ams, first, c, dev, stream, ev_start(), ev_stop());
+        rc = launch_table(shared, gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop());
     }
     return rc;
 }
@@ -496,7 +515,7 @@ int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *st
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
     const int rc =
-        submit_updates(solo, shared, nullptr, nullptr, gdt, o.amsgrad != 0, *step == 0, c, dev, stream, timing);
+        submit_updates(solo, shared, nullptr, nullptr, gdt, o.amsgrad != 0, *step == 0, c, nullptr, dev, stream, timing);
     if (rc != RADAMW_OK) return rc;
     *step += 1;
     *updated = 1;
@@ -563,9 +582,10 @@ int plan(int64_t rows, int64_t *scratch_elements, int32_t *extra) {
     return RADAMW_OK;
 }
 
-// Launch the merges for already validated arguments.
-int merge_launch(const StatsRec *rows, int64_t nrows, StatsRec *scratch, StatsRec *report,
-                 bool hierarchical, hipStream_t stream) {
+// The fan-in-1024 levels (hierarchical only) for already validated
+// arguments: *cur / *count receive the records the final merge reduces.
+int merge_levels(const StatsRec *rows, int64_t nrows, StatsRec *scratch, bool hierarchical, hipStream_t stream,
+                 const StatsRec **cur_out, int64_t *count_out) {
     const StatsRec *cur = rows;
     int64_t count = nrows;
     if (hierarchical) {
@@ -580,7 +600,19 @@ int merge_launch(const StatsRec *rows, int64_t nrows, StatsRec *scratch, StatsRe
             level += blocks;
         }
     }
-    int rc = hip_status(launch_merge(cur, count, count, 1, report, stream));
+    *cur_out = cur;
+    *count_out = count;
+    return RADAMW_OK;
+}
+
+// Launch the merges for already validated arguments.
+int merge_launch(const StatsRec *rows, int64_t nrows, StatsRec *scratch, StatsRec *report,
+                 bool hierarchical, hipStream_t stream) {
+    const StatsRec *cur;
+    int64_t count;
+    int rc = merge_levels(rows, nrows, scratch, hierarchical, stream, &cur, &count);
+    if (rc) return rc;
+    rc = hip_status(launch_merge(cur, count, count, 1, report, stream));
     if (rc) return rc;
     g_launches.fetch_add(1, std::memory_order_relaxed);
     return RADAMW_OK;
@@ -648,42 +680,108 @@ std::vector<char> build_stats_table(const std::vector<StatsSeg> &st, int64_t nro
     return bytes;
 }
 
-// Host memory mapped for the device that receives the final merge, so the
-// stream synchronisation after it is the whole read-back (report_mu held).
-int ensure_mapped(DeviceCache &dc) {
+// The per-device page of host memory mapped for the device, which receives
+// the final merge's report and decision, and the event that marks the
+// merge's completion (report_mu held).
+int ensure_mapped(DeviceCache &dc, int dev) {
     if (dc.mapped_report_host) return RADAMW_OK;
+    DeviceScope scope(dev);
     void *hp = nullptr, *dp = nullptr;
     hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) return hip_status(e);
     e = hipHostGetDevicePointer(&dp, hp, 0);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&dc.merge_done, hipEventDisableTiming);
     if (e != hipSuccess) {
+        dc.merge_done = nullptr;
         (void)hipHostFree(hp);
         return hip_status(e);
     }
     dc.mapped_report_host = static_cast<radamw_stats *>(hp);
     dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
+    dc.mapped_decision_host = reinterpret_cast<Decision *>(static_cast<char *>(hp) + 16);
+    dc.mapped_decision_dev = reinterpret_cast<Decision *>(static_cast<char *>(dp) + 16);
     return RADAMW_OK;
 }
 
-// Synchronise the stream and copy the mapped report out (report_mu held).
-int read_mapped(DeviceCache &dc, hipStream_t stream, radamw_stats *host) {
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_status(e);
-    std::memcpy(host, dc.mapped_report_host, sizeof *host);
-    return RADAMW_OK;
-}
-
-// Merge the rows and read the 12-byte report back.
-int report_to_host(const StatsRec *rows, int64_t nrows, StatsRec *scratch, bool hierarchical, int dev,
-                   hipStream_t stream, radamw_stats *host) {
+// The tail of every fused step, under the device's report lock:
+//   prepare(&cur, &count)  launches whatever merges leave `count` records at
+//                          `cur` for the final merge;
+//   the final merge reduces them, takes the skip / clip decision on the
+//   device and writes report and decision into the mapped page, and the
+//   decision also to dec_dev, where the update kernels read it;
+//   submit()               queues the update launches right behind it;
+// only then does the host wait, for the merge alone, and read the page.  The
+// GPU goes from the merge to the updates without waiting for the host.
+template <typename Prepare, typename Submit>
+int fused_tail(int dev, hipStream_t stream, Decision *dec_dev, const DecideArgs &args, radamw_stats *host,
+               Decision *host_dec, Prepare prepare, Submit submit) {
     DeviceCache &dc = g_devices[dev];
     std::lock_guard<std::mutex> lock(dc.report_mu);
-    int rc = ensure_mapped(dc);
+    int rc = ensure_mapped(dc, dev);
     if (rc) return rc;
-    if ((rc = merge_launch(rows, nrows, scratch, reinterpret_cast<StatsRec *>(dc.mapped_report_dev), hierarchical,
-                           stream)))
-        return rc;
-    return read_mapped(dc, stream, host);
+    const StatsRec *cur = nullptr;
+    int64_t count = 0;
+    if ((rc = prepare(&cur, &count))) return rc;
+    rc = hip_status(launch_merge_decide(cur, count, reinterpret_cast<StatsRec *>(dc.mapped_report_dev), dec_dev,
+                                        dc.mapped_decision_dev, args, stream));
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    hipError_t e = hipEventRecord(dc.merge_done, stream);
+    if (e != hipSuccess) return hip_status(e);
+    const int submitted = submit();
+    e = hipEventSynchronize(dc.merge_done);
+    if (e != hipSuccess) return hip_status(e);
+    std::memcpy(host, dc.mapped_report_host, sizeof *host);
+    std::memcpy(host_dec, dc.mapped_decision_host, sizeof *host_dec);
+    return submitted;
+}
+
+// The decision of TR-zh from a report on the host (radamw_decide).
+int decide_host(const radamw_stats *host_report, double gradient_scale, double max_grad_norm,
+                radamw_control *ctrl, radamw_fused_result *result) {
+    if (!host_report || !ctrl || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    int rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    double sumsq;
+    uint32_t count;
+    decode(*host_report, &sumsq, &count);
+    const double norm = std::sqrt(sumsq) / gradient_scale;
+    double clip = 1.0;
+    if (max_grad_norm > 0.0) clip = std::min(1.0, max_grad_norm / (norm + 1e-6));
+    // a skipped step applies no clip: the scale passes through unchanged
+    ctrl->skip_update = count > 0 ? 1 : 0;
+    ctrl->gradient_scale = (count > 0 || clip == 1.0) ? gradient_scale : gradient_scale / clip;
+    if (result) {
+        result->found_inf = count > 0 ? 1 : 0;
+        result->nonfinite = count;
+        result->reserved = 0;
+        result->sumsq = sumsq;
+        result->total_norm = norm;
+        result->clip_coef = clip;
+    }
+    return RADAMW_OK;
+}
+
+// The host's decision from the report it read, which must be the device's:
+// the same skip, and the same FP32 unscale factor for an update.  Fills the
+// result; *updated tells whether the queued kernels wrote anything.
+int settle(const radamw_stats &host, const Decision &dev_dec, double gradient_scale, double max_grad_norm,
+           radamw_fused_result *result, bool *updated) {
+    radamw_control ctrl;
+    int rc = decide_host(&host, gradient_scale, max_grad_norm, &ctrl, result);
+    if (rc) return rc;
+    const bool skip = ctrl.skip_update != 0;
+    const float inv = static_cast<float>(1.0 / ctrl.gradient_scale);
+    uint32_t a, b;
+    std::memcpy(&a, &inv, 4);
+    std::memcpy(&b, &dev_dec.inv_scale, 4);
+    if (skip != (dev_dec.skip != 0) || (!skip && a != b)) {
+        g_last_hip = static_cast<int>(hipErrorUnknown);  // a library fault: the two decisions must agree
+        return RADAMW_ERR_HIP;
+    }
+    result->updated = skip ? 0 : 1;
+    *updated = !skip;
+    return RADAMW_OK;
 }
 
 }  // namespace
@@ -705,9 +803,9 @@ struct radamw_list_s {
     std::vector<StatsSeg> st; // statistics rows of the non-empty gradients
     int64_t nrows = 0;
     size_t stats_coarse_off = 0;
-    char *mem = nullptr;      // device: [update table][stats table][rows][merge scratch]
+    char *mem = nullptr;      // device: [update table][stats table][rows][merge scratch][decision]
     char *staging = nullptr;  // pinned host copy of the tables, the source of their upload
-    size_t table_off = 0, stats_off = 0, rows_off = 0;
+    size_t table_off = 0, stats_off = 0, rows_off = 0, dec_off = 0;
     hipEvent_t done = nullptr;  // recorded after the last launch that reads `mem`
     bool pending = false;
 };
@@ -715,19 +813,6 @@ struct radamw_list_s {
 namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Temporarily make `dev` the calling thread's current device.
-struct DeviceScope {
-    int prev = -1;
-    explicit DeviceScope(int dev) {
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        if (prev != dev) (void)hipSetDevice(dev);
-    }
-    ~DeviceScope() {
-        int cur = -1;
-        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-    }
-};
 
 // Checks shared by the list's step entry points.
 int list_step_checks(radamw_list_s *l, const radamw_options *opts, const uint64_t *step, hipStream_t stream) {
@@ -742,19 +827,24 @@ int list_step_checks(radamw_list_s *l, const radamw_options *opts, const uint64_
     return RADAMW_OK;
 }
 
-// The update launches of one list step, then the event that guards `mem`.
-int list_update(radamw_list_s *l, uint64_t *step, const radamw_options &o, double gradient_scale,
-                hipStream_t stream, UpdateTiming timing) {
-    const Coefs c = make_coefs(o, *step + 1, gradient_scale);
-    int rc = submit_updates(l->solo, l->shared, l->shared.size() > 1 ? &l->table : nullptr, l->mem + l->table_off,
-                            l->gdt, l->amsgrad, *step == 0, c, l->dev, stream, timing);
-    if (rc) return rc;
+// The update launches of one list step (reading `dec` when a fused step
+// decides on the device); the caller records the list's event after them.
+int list_launch(radamw_list_s *l, uint64_t step, const radamw_options &o, double gradient_scale,
+                const Decision *dec, hipStream_t stream, UpdateTiming timing) {
+    const Coefs c = make_coefs(o, step + 1, gradient_scale);
+    return submit_updates(l->solo, l->shared, l->shared.size() > 1 ? &l->table : nullptr, l->mem + l->table_off,
+                          l->gdt, l->amsgrad, step == 0, c, dec, l->dev, stream, timing);
+}
+
+// Record the event that guards the list's memory after its last launch.
+int list_mark(radamw_list_s *l, hipStream_t stream) {
     hipError_t e = hipEventRecord(l->done, stream);
     if (e != hipSuccess) return hip_status(e);
     l->pending = true;
-    *step += 1;
     return RADAMW_OK;
 }
+
+Decision *list_decision(radamw_list_s *l) { return reinterpret_cast<Decision *>(l->mem + l->dec_off); }
 
 StatsRec *list_rows(radamw_list_s *l) { return reinterpret_cast<StatsRec *>(l->mem + l->rows_off); }
 
@@ -850,7 +940,7 @@ int radamw_step(const float *p, const void *g, radamw_dtype gdt, int64_t n, cons
         const Coefs c = make_coefs(*opts, in->step + 1, ctrl->gradient_scale);
         const UpdateTiming timing = g_timing;
         g_timing = UpdateTiming{};
-        if ((rc = launch_single(d, gdt, ams, first, c, dev, stream, timing.start, timing.stop))) return rc;
+        if ((rc = launch_single(d, gdt, ams, first, c, nullptr, dev, stream, timing.start, timing.stop))) return rc;
         out->step = in->step + 1;
         *updated = 1;
         return RADAMW_OK;
@@ -1059,27 +1149,7 @@ int radamw_read_report(const radamw_stats *report, radamw_stats *host_report, ra
 
 int radamw_decide(const radamw_stats *host_report, double gradient_scale, double max_grad_norm,
                   radamw_control *ctrl, radamw_fused_result *result) {
-    if (!host_report || !ctrl || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
-    int rc;
-    if ((rc = check_scale(gradient_scale))) return rc;
-    double sumsq;
-    uint32_t count;
-    decode(*host_report, &sumsq, &count);
-    const double norm = std::sqrt(sumsq) / gradient_scale;
-    double clip = 1.0;
-    if (max_grad_norm > 0.0) clip = std::min(1.0, max_grad_norm / (norm + 1e-6));
-    // a skipped step applies no clip: the scale passes through unchanged
-    ctrl->skip_update = count > 0 ? 1 : 0;
-    ctrl->gradient_scale = (count > 0 || clip == 1.0) ? gradient_scale : gradient_scale / clip;
-    if (result) {
-        result->found_inf = count > 0 ? 1 : 0;
-        result->nonfinite = count;
-        result->reserved = 0;
-        result->sumsq = sumsq;
-        result->total_norm = norm;
-        result->clip_coef = clip;
-    }
-    return RADAMW_OK;
+    return decide_host(host_report, gradient_scale, max_grad_norm, ctrl, result);
 }
 
 int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt) {
@@ -1159,18 +1229,29 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
             });
         if (rc) return rc;
     }
+    // the update launches are queued behind the final merge and read its
+    // decision from the workspace's last 12 bytes
+    Decision *dec_dev = reinterpret_cast<Decision *>(static_cast<char *>(workspace) + need - 12);
+    std::vector<SegDesc> solo, shared;
+    split_launches(inplace_descs(segs, nseg, nullptr, 0), solo, shared);
+    const Coefs c = make_coefs(*opts, *step + 1, gradient_scale);
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
     radamw_stats host;
-    if ((rc = report_to_host(rows, nrows, rows + nrows, hierarchical != 0, dev, stream, &host))) return rc;
-    radamw_control ctrl;
-    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
-    if (ctrl.skip_update) {
-        result->updated = 0;
-        return RADAMW_OK;
-    }
-    int32_t updated = 0;
-    rc = multi_update(segs, nseg, gdt, step, *opts, ctrl.gradient_scale, dev, stream, &updated);
+    Decision dd;
+    rc = fused_tail(
+        dev, stream, dec_dev, DecideArgs{gradient_scale, max_grad_norm}, &host, &dd,
+        [&](const StatsRec **cur, int64_t *count) {
+            return merge_levels(rows, nrows, rows + nrows, hierarchical != 0, stream, cur, count);
+        },
+        [&]() {
+            return submit_updates(solo, shared, nullptr, nullptr, gdt, opts->amsgrad != 0, *step == 0, c, dec_dev,
+                                  dev, stream, timing);
+        });
     if (rc) return rc;
-    result->updated = updated;
+    bool updated = false;
+    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    if (updated) *step += 1;
     return RADAMW_OK;
 }
 
@@ -1208,7 +1289,8 @@ int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gd
     l->table_off = 0;
     l->stats_off = align_up(l->table.bytes.size(), 256);
     l->rows_off = align_up(l->stats_off + stats_table.size(), 256);
-    const size_t total = l->rows_off + static_cast<size_t>(l->nrows) * 12 + static_cast<size_t>(se) * 4;
+    l->dec_off = align_up(l->rows_off + static_cast<size_t>(l->nrows) * 12 + static_cast<size_t>(se) * 4, 16);
+    const size_t total = l->dec_off + 16;
     DeviceScope scope(dev);
     bool copying = false;
     auto fail = [&](hipError_t e) {
@@ -1262,7 +1344,9 @@ int radamw_list_step(radamw_list list, uint64_t *step, const radamw_options *opt
     if ((rc = list_wait(list, stream))) return rc;
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
-    if ((rc = list_update(list, step, *opts, ctrl->gradient_scale, stream, timing))) return rc;
+    if ((rc = list_launch(list, *step, *opts, ctrl->gradient_scale, nullptr, stream, timing))) return rc;
+    if ((rc = list_mark(list, stream))) return rc;
+    *step += 1;
     *updated = 1;
     return RADAMW_OK;
 }
@@ -1282,20 +1366,26 @@ int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_option
     if (list->active == 0) return RADAMW_OK;
     if ((rc = list_wait(list, stream))) return rc;
     if ((rc = list_analyze(list, stream))) return rc;
-    radamw_stats host;
     StatsRec *rows = list_rows(list);
-    if ((rc = report_to_host(rows, list->nrows, rows + list->nrows, hierarchical != 0, list->dev, stream, &host)))
-        return rc;
-    radamw_control ctrl;
-    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
-    if (ctrl.skip_update) {
-        result->updated = 0;
-        return RADAMW_OK;
-    }
+    Decision *dec_dev = list_decision(list);
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
-    if ((rc = list_update(list, step, *opts, ctrl.gradient_scale, stream, timing))) return rc;
-    result->updated = 1;
+    radamw_stats host;
+    Decision dd;
+    rc = fused_tail(
+        list->dev, stream, dec_dev, DecideArgs{gradient_scale, max_grad_norm}, &host, &dd,
+        [&](const StatsRec **cur, int64_t *count) {
+            return merge_levels(rows, list->nrows, rows + list->nrows, hierarchical != 0, stream, cur, count);
+        },
+        [&]() {
+            int r = list_launch(list, *step, *opts, gradient_scale, dec_dev, stream, timing);
+            const int m = list_mark(list, stream);
+            return r ? r : m;
+        });
+    if (rc) return rc;
+    bool updated = false;
+    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    if (updated) *step += 1;
     return RADAMW_OK;
 }
 
@@ -1330,57 +1420,67 @@ int radamw_lists_fused_step(const radamw_list *lists, int32_t nlists, uint64_t *
         if ((rc = list_wait(lists[k], stream))) return rc;
     for (int32_t k : act)
         if ((rc = list_analyze(lists[k], stream))) return rc;
-    radamw_stats host;
-    if (act.size() == 1) {
-        radamw_list_s *l = lists[act[0]];
-        StatsRec *rows = list_rows(l);
-        if ((rc = report_to_host(rows, l->nrows, rows + l->nrows, hierarchical != 0, dev, stream, &host))) return rc;
-    } else {
-        // each list's rows reduce to one record; the records, in call
-        // order, take one final merge into the mapped report
-        DeviceCache &dc = g_devices[dev];
-        std::lock_guard<std::mutex> lock(dc.report_mu);
-        if ((rc = ensure_mapped(dc))) return rc;
-        const int64_t nact = static_cast<int64_t>(act.size());
-        if (dc.group_cap < nact) {
-            DeviceScope scope(dev);
-            if (dc.group_rec) (void)hipFree(dc.group_rec);
-            dc.group_rec = nullptr;
-            dc.group_cap = 0;
-            const int64_t cap = std::max<int64_t>(nact, 256);
-            hipError_t e = hipMalloc(&dc.group_rec, static_cast<size_t>(cap) * sizeof(StatsRec));
-            if (e != hipSuccess) {
-                dc.group_rec = nullptr;
-                return hip_status(e);
-            }
-            dc.group_cap = cap;
-        }
-        for (int64_t i = 0; i < nact; ++i) {
-            radamw_list_s *l = lists[act[i]];
-            StatsRec *rows = list_rows(l);
-            if ((rc = merge_launch(rows, l->nrows, rows + l->nrows, dc.group_rec + i, hierarchical != 0, stream)))
-                return rc;
-        }
-        rc = hip_status(launch_merge(dc.group_rec, nact, nact, 1, reinterpret_cast<StatsRec *>(dc.mapped_report_dev),
-                                     stream));
-        if (rc) return rc;
-        g_launches.fetch_add(1, std::memory_order_relaxed);
-        if ((rc = read_mapped(dc, stream, &host))) return rc;
-    }
-    radamw_control ctrl;
-    radamw_decide(&host, gradient_scale, max_grad_norm, &ctrl, result);
-    if (ctrl.skip_update) {
-        result->updated = 0;
-        return RADAMW_OK;
-    }
+    // every list's update reads the decision from the first active list's
+    // slot, so every list's event is recorded after the step's last launch
+    Decision *dec_dev = list_decision(lists[act[0]]);
+    DeviceCache &dc = g_devices[dev];
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
-    for (size_t i = 0; i < act.size(); ++i) {
-        const int32_t k = act[i];
-        const UpdateTiming t{i == 0 ? timing.start : nullptr, i + 1 == act.size() ? timing.stop : nullptr};
-        if ((rc = list_update(lists[k], &steps[k], opts[k], ctrl.gradient_scale, stream, t))) return rc;
-    }
-    result->updated = 1;
+    radamw_stats host;
+    Decision dd;
+    rc = fused_tail(
+        dev, stream, dec_dev, DecideArgs{gradient_scale, max_grad_norm}, &host, &dd,
+        [&](const StatsRec **cur, int64_t *count) -> int {
+            if (act.size() == 1) {
+                radamw_list_s *l = lists[act[0]];
+                StatsRec *rows = list_rows(l);
+                return merge_levels(rows, l->nrows, rows + l->nrows, hierarchical != 0, stream, cur, count);
+            }
+            // each list's rows reduce to one record; the records, in call
+            // order, take the final merge (report_mu is held)
+            const int64_t nact = static_cast<int64_t>(act.size());
+            if (dc.group_cap < nact) {
+                DeviceScope scope(dev);
+                if (dc.group_rec) (void)hipFree(dc.group_rec);
+                dc.group_rec = nullptr;
+                dc.group_cap = 0;
+                const int64_t cap = std::max<int64_t>(nact, 256);
+                hipError_t e = hipMalloc(&dc.group_rec, static_cast<size_t>(cap) * sizeof(StatsRec));
+                if (e != hipSuccess) {
+                    dc.group_rec = nullptr;
+                    return hip_status(e);
+                }
+                dc.group_cap = cap;
+            }
+            for (int64_t i = 0; i < nact; ++i) {
+                radamw_list_s *l = lists[act[i]];
+                StatsRec *rows = list_rows(l);
+                const int r = merge_launch(rows, l->nrows, rows + l->nrows, dc.group_rec + i, hierarchical != 0,
+                                           stream);
+                if (r) return r;
+            }
+            *cur = dc.group_rec;
+            *count = nact;
+            return RADAMW_OK;
+        },
+        [&]() -> int {
+            int r = RADAMW_OK;
+            for (size_t i = 0; i < act.size() && r == RADAMW_OK; ++i) {
+                const int32_t k = act[i];
+                const UpdateTiming t{i == 0 ? timing.start : nullptr, i + 1 == act.size() ? timing.stop : nullptr};
+                r = list_launch(lists[k], steps[k], opts[k], gradient_scale, dec_dev, stream, t);
+            }
+            for (int32_t k : act) {
+                const int m = list_mark(lists[k], stream);
+                if (r == RADAMW_OK) r = m;
+            }
+            return r;
+        });
+    if (rc) return rc;
+    bool updated = false;
+    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    if (updated)
+        for (int32_t k : act) steps[k] += 1;
     return RADAMW_OK;
 }
 

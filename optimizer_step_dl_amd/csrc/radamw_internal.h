@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <cstddef>
 #include <cstdint>
 
 namespace radamw {
@@ -111,6 +112,25 @@ struct StatsRec {
     uint32_t w[3];
 };
 
+// The skip / clip decision of a fused step, taken on the device by the final
+// merge so that the update kernels can be queued before the host has read
+// the report back: skip != 0 when the report counts a non-finite value;
+// otherwise inv_scale, given the sign of the kernel's own Coefs::inv_scale
+// (maximize), replaces the update's unscale factor.
+struct Decision {
+    uint32_t skip;
+    float inv_scale;  // (float)(1 / (gradient_scale / clip)), clip folded in
+};
+static_assert(sizeof(Decision) == 8 && offsetof(Decision, inv_scale) == 4,
+              "the update kernels load a decision as two 32-bit words");
+
+// What the final merge needs to decide: the caller's scale and the clip
+// bound (<= 0: no clipping).
+struct DecideArgs {
+    double gradient_scale;
+    double max_grad_norm;
+};
+
 // Global-address-space views of generic pointers.  Tensor pointers that
 // reach a kernel through memory (the multi-tensor descriptor table) are
 // generic to the compiler, which would then emit FLAT instructions; these
@@ -128,13 +148,16 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gl(T *p) {
 // hipError_t of the launch.
 // start / stop (may be null) are recorded at the kernel's start and end
 // (hipExtLaunchKernelGGL), for measurement.
-hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
-                                bool first, int grid, hipStream_t stream, hipEvent_t start,
+// dec (device, may be null): a decision the kernels read before storing; a
+// skip decision leaves every buffer unwritten, otherwise its inv_scale
+// replaces c.inv_scale.
+hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, const Decision *dec, int gdt,
+                                bool amsgrad, bool first, int grid, hipStream_t stream, hipEvent_t start,
                                 hipEvent_t stop);
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
-                               const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
-                               hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                               const Coefs &c, const Decision *dec, int gdt, bool amsgrad, bool first,
+                               int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 // One gradient of a multi-tensor statistics launch: its records are
 // out[row_begin, row_begin + rows), laid out exactly as a single-tensor
 // launch would write them.
@@ -156,5 +179,9 @@ hipError_t launch_analyze_table(const StatsSeg *segs_dev, const int32_t *coarse_
                                 int gdt, StatsRec *out, hipStream_t stream);
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
                         StatsRec *out, hipStream_t stream);
+// The final merge of a fused step: one workgroup reduces all nin records,
+// writes the report to `out` and the decision to dec_dev and dec_host.
+hipError_t launch_merge_decide(const StatsRec *in, int64_t nin, StatsRec *out, Decision *dec_dev,
+                               Decision *dec_host, const DecideArgs &a, hipStream_t stream);
 
 }  // namespace radamw

@@ -112,16 +112,22 @@ __device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
     return v;
 }
 
-__device__ __forceinline__ void write_record(StatsRec *out, double s, uint64_t count) {
+__device__ __forceinline__ StatsRec write_record(StatsRec *out, double s, uint64_t count) {
     const uint64_t bits = __builtin_bit_cast(uint64_t, s);
-    out->w[0] = uint32_t(bits);
-    out->w[1] = uint32_t(bits >> 32);
-    out->w[2] = count > 0xffffffffull ? 0xffffffffu : uint32_t(count);
+    StatsRec r;
+    r.w[0] = uint32_t(bits);
+    r.w[1] = uint32_t(bits >> 32);
+    r.w[2] = count > 0xffffffffull ? 0xffffffffu : uint32_t(count);
+    out->w[0] = r.w[0];
+    out->w[1] = r.w[1];
+    out->w[2] = r.w[2];
+    return r;
 }
 
-// Fixed-order workgroup reduction; lane 0 writes the record.
+// Fixed-order workgroup reduction; thread 0 writes the record and returns
+// it (other threads return an unspecified record).
 template <int BLOCK>
-__device__ __forceinline__ void block_finish(double s, uint64_t count, StatsRec *out) {
+__device__ __forceinline__ StatsRec block_finish(double s, uint64_t count, StatsRec *out) {
     constexpr int WAVES = BLOCK / 64;
     __shared__ double ws[WAVES];
     __shared__ uint64_t wc[WAVES];
@@ -133,6 +139,7 @@ __device__ __forceinline__ void block_finish(double s, uint64_t count, StatsRec 
         wc[wave] = count;
     }
     __syncthreads();
+    StatsRec rec{};
     if (threadIdx.x == 0) {
         double total = 0.0;
         uint64_t c = 0;
@@ -140,8 +147,9 @@ __device__ __forceinline__ void block_finish(double s, uint64_t count, StatsRec 
             total += ws[w];
             c += wc[w];
         }
-        write_record(out, total, c);
+        rec = write_record(out, total, c);
     }
+    return rec;
 }
 
 // Row r of one gradient's analysis: elements [0, head) and the tail after
@@ -228,6 +236,70 @@ __global__ __launch_bounds__(MERGE_BLOCK) void stats_merge(const StatsRec *in, i
     block_finish<MERGE_BLOCK>(s, c, out + blockIdx.x);
 }
 
+// Correctly rounded binary64 square root: the hardware estimate, then
+// Tuckerman's test on its neighbours (y is the rounded root of x exactly
+// when y * pred(y) < x <= y * succ(y); fma gives each product's difference
+// from x with its exact sign).  The host's sqrt is correctly rounded, so
+// both sides take the same decision from the same report.
+__device__ __forceinline__ double sqrt_rn(double x) {
+    if (!(x > 0.0)) return x;  // 0 (a sum of squares is never negative)
+    double y = __builtin_sqrt(x);
+    const uint64_t b = __builtin_bit_cast(uint64_t, y);
+    const double below = __builtin_bit_cast(double, b - 1), above = __builtin_bit_cast(double, b + 1);
+    if (__builtin_fma(y, below, -x) >= 0.0) y = below;
+    else if (__builtin_fma(y, above, -x) < 0.0) y = above;
+    return y;
+}
+
+// The fused step's decision from the merged report (TR-zh "在 ruda:0 上进行
+// 原生 PyTorch 训练": a non-finite value skips the step, otherwise the global
+// norm of the unscaled gradients is clipped), in the operation order of the
+// host's radamw_decide and make_coefs: norm = sqrt(sumsq) / scale, clip =
+// min(1, max_norm / (norm + 1e-6)), inv_scale = (float)(1 / (scale /
+// clip)) before the sign of maximize is applied.  Every binary64 operation
+// is correctly rounded on both sides.
+__device__ Decision decide_on_device(double sumsq, uint32_t count, const DecideArgs &a) {
+#pragma clang fp contract(off)
+    Decision d;
+    if (count > 0) {
+        d.skip = 1;
+        d.inv_scale = static_cast<float>(1.0 / a.gradient_scale);
+        return d;
+    }
+    const double norm = sqrt_rn(sumsq) / a.gradient_scale;
+    double clip = 1.0;
+    if (a.max_grad_norm > 0.0) {
+        const double q = a.max_grad_norm / (norm + 1e-6);
+        clip = q < 1.0 ? q : 1.0;
+    }
+    const double eff = clip == 1.0 ? a.gradient_scale : a.gradient_scale / clip;
+    d.skip = 0;
+    d.inv_scale = static_cast<float>(1.0 / eff);
+    return d;
+}
+
+// Final merge of a fused step (one workgroup): the report goes to `out` and
+// the decision, taken from the report's own bits, to both dec pointers.
+__global__ __launch_bounds__(MERGE_BLOCK) void stats_merge_decide(const StatsRec *in, int64_t nin, StatsRec *out,
+                                                                  Decision *dec_dev, Decision *dec_host,
+                                                                  DecideArgs a) {
+    double s = 0.0;
+    uint64_t c = 0;
+    for (int64_t r = threadIdx.x; r < nin; r += MERGE_BLOCK) {
+        const StatsRec rec = in[r];
+        s += __builtin_bit_cast(double, uint64_t(rec.w[0]) | (uint64_t(rec.w[1]) << 32));
+        c += rec.w[2];
+    }
+    const StatsRec rec = block_finish<MERGE_BLOCK>(s, c, out);
+    if (threadIdx.x == 0) {
+        // decide from exactly the words of the report
+        const Decision d = decide_on_device(
+            __builtin_bit_cast(double, uint64_t(rec.w[0]) | (uint64_t(rec.w[1]) << 32)), rec.w[2], a);
+        *dec_dev = d;
+        *dec_host = d;
+    }
+}
+
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream) {
     switch (gdt) {
@@ -261,6 +333,13 @@ hipError_t launch_analyze_table(const StatsSeg *segs_dev, const int32_t *coarse_
 hipError_t launch_merge(const StatsRec *in, int64_t nin, int64_t per_block, int64_t nblocks,
                         StatsRec *out, hipStream_t stream) {
     hipLaunchKernelGGL(stats_merge, dim3(nblocks), dim3(MERGE_BLOCK), 0, stream, in, nin, per_block, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_decide(const StatsRec *in, int64_t nin, StatsRec *out, Decision *dec_dev,
+                               Decision *dec_host, const DecideArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(stats_merge_decide, dim3(1), dim3(MERGE_BLOCK), 0, stream, in, nin, out, dec_dev, dec_host,
+                       a);
     return hipGetLastError();
 }
 

@@ -130,9 +130,30 @@ __device__ __forceinline__ void scalar_element(const SegDesc &s, int64_t e, cons
 // One tile of a mutually aligned segment: UPDATE_UNROLL 16-byte chunks per
 // lane, loads first, then arithmetic and stores.  The last tile of the
 // segment also handles the <= 3 head and <= 3 tail elements with scalar code.
+// A fused step's decision, if any: `skip` and the clipped unscale factor,
+// which takes the sign of the launch's own factor (maximize negates).  The
+// load is uniform (one scalar load per workgroup, from L2).  Negation is
+// exact and rounding to nearest even is symmetric, so the result has the
+// bits of the host's (float)(sign / scale).
+__device__ __forceinline__ bool read_decision(const Decision *dec, Coefs &c) {
+    if (!dec) return false;
+    const u32x2 d = *gl(reinterpret_cast<const u32x2 *>(dec));  // {skip, inv_scale bits}
+    // the words go through scalars: this compiler lowers __builtin_bit_cast
+    // of a vector element lvalue (d.y) to the vector's first element
+    const uint32_t skip = d.x, inv_bits = d.y;
+    c.inv_scale = __builtin_copysignf(__builtin_bit_cast(float, inv_bits), c.inv_scale);
+    return skip != 0;
+}
+
+// Keeps the compiler from moving the tile's loads below, or the decision's
+// load above, this point: the data loads go out first and the decision's
+// latency hides behind them.
+__device__ __forceinline__ void loads_issued() { asm volatile("" ::: "memory"); }
+
 template <int GDT, bool AMS, bool FIRST>
-__device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, const Coefs &c) {
+__device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, const Coefs &c0, const Decision *dec) {
     constexpr int U = UPDATE_UNROLL;
+    Coefs c = c0;
     const int tid = threadIdx.x;
     const int64_t head = s.head;
     const int64_t body = (s.n - head) >> 2;  // 16-byte chunks in the aligned body
@@ -181,6 +202,8 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
                 M[u] = f32x4(0.0f); V[u] = f32x4(0.0f); X[u] = f32x4(0.0f);
             }
         }
+        loads_issued();
+        if (read_decision(dec, c)) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = base + int64_t(u) * UPDATE_BLOCK + tid;
@@ -192,6 +215,7 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
             if constexpr (AMS) stream_store(x_out + k, X[u]);
         }
     } else {
+        if (read_decision(dec, c)) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = base + int64_t(u) * UPDATE_BLOCK + tid;
@@ -227,7 +251,9 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
 // One tile of a segment whose streams are not mutually 16-byte aligned
 // (only possible for views at odd offsets): plain element-wise code.
 template <int GDT, bool AMS, bool FIRST>
-__device__ __forceinline__ void scalar_tile(const SegDesc &s, int64_t tile, const Coefs &c) {
+__device__ __forceinline__ void scalar_tile(const SegDesc &s, int64_t tile, const Coefs &c0, const Decision *dec) {
+    Coefs c = c0;
+    if (read_decision(dec, c)) return;
     const int64_t base = tile * UPDATE_TILE_ELEMS;
 #pragma unroll 4
     for (int k = 0; k < 4 * UPDATE_UNROLL; ++k) {
@@ -237,18 +263,18 @@ __device__ __forceinline__ void scalar_tile(const SegDesc &s, int64_t tile, cons
 }
 
 template <int GDT, bool AMS, bool FIRST>
-__device__ __forceinline__ void any_tile(const SegDesc &s, int64_t tile, const Coefs &c) {
+__device__ __forceinline__ void any_tile(const SegDesc &s, int64_t tile, const Coefs &c, const Decision *dec) {
     if (s.head >= 0)
-        vector_tile<GDT, AMS, FIRST>(s, tile, c);
+        vector_tile<GDT, AMS, FIRST>(s, tile, c, dec);
     else
-        scalar_tile<GDT, AMS, FIRST>(s, tile, c);
+        scalar_tile<GDT, AMS, FIRST>(s, tile, c, dec);
 }
 
 // One tensor: the descriptor travels in the kernel arguments; workgroup t
 // handles tile t (the host launches exactly one workgroup per tile).
 template <int GDT, bool AMS, bool FIRST>
-__global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, Coefs c) {
-    any_tile<GDT, AMS, FIRST>(s, blockIdx.x, c);
+__global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, Coefs c, const Decision *dec) {
+    any_tile<GDT, AMS, FIRST>(s, blockIdx.x, c, dec);
 }
 
 // A list of tensors in one launch.  Descriptors, tile prefix sums and a
@@ -260,7 +286,7 @@ __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_single(SegDesc s, C
 template <int GDT, bool AMS, bool FIRST>
 __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_table(
     const SegDesc *__restrict__ segs, const int64_t *__restrict__ prefix,
-    const int32_t *__restrict__ coarse, Coefs c) {
+    const int32_t *__restrict__ coarse, Coefs c, const Decision *dec) {
     const int64_t t = blockIdx.x;  // one workgroup per tile, grid == total_tiles
     const int64_t j = t >> TABLE_COARSE_LOG2;
     int32_t lo = coarse[j], hi = coarse[j + 1] + 1;  // prefix[lo] <= t < prefix[hi]
@@ -269,25 +295,25 @@ __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_table(
         if (prefix[mid] <= t) lo = mid; else hi = mid;
     }
     const SegDesc seg = segs[lo];
-    any_tile<GDT, AMS, FIRST>(seg, t - prefix[lo], c);
+    any_tile<GDT, AMS, FIRST>(seg, t - prefix[lo], c, dec);
 }
 
 template <int GDT, bool AMS, bool FIRST>
-static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, int grid, hipStream_t st,
-                                  hipEvent_t start, hipEvent_t stop) {
+static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, const Decision *dec, int grid,
+                                  hipStream_t st, hipEvent_t start, hipEvent_t stop) {
     hipExtLaunchKernelGGL((adamw_update_single<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
-                          st, start, stop, 0, seg, c);
+                          st, start, stop, 0, seg, c, dec);
     return hipGetLastError();
 }
 
 template <int GDT, bool AMS, bool FIRST>
 static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, const int32_t *coarse,
-                                 int32_t nseg, int64_t total, const Coefs &c, int grid, hipStream_t st,
-                                 hipEvent_t start, hipEvent_t stop) {
+                                 int32_t nseg, int64_t total, const Coefs &c, const Decision *dec, int grid,
+                                 hipStream_t st, hipEvent_t start, hipEvent_t stop) {
     (void)nseg;
     (void)total;
     hipExtLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
-                          st, start, stop, 0, segs, prefix, coarse, c);
+                          st, start, stop, 0, segs, prefix, coarse, c, dec);
     return hipGetLastError();
 }
 
@@ -308,17 +334,17 @@ static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, con
     default: return hipErrorInvalidValue;                                             \
     }
 
-hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, int gdt, bool amsgrad,
-                                bool first, int grid, hipStream_t stream, hipEvent_t start,
+hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, const Decision *dec, int gdt,
+                                bool amsgrad, bool first, int grid, hipStream_t stream, hipEvent_t start,
                                 hipEvent_t stop) {
-    RADAMW_DISPATCH(launch_single_t, seg, c, grid, stream, start, stop)
+    RADAMW_DISPATCH(launch_single_t, seg, c, dec, grid, stream, start, stop)
 }
 
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
-                               const Coefs &c, int gdt, bool amsgrad, bool first, int grid,
-                               hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, nseg, total_tiles, c, grid,
+                               const Coefs &c, const Decision *dec, int gdt, bool amsgrad, bool first,
+                               int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, nseg, total_tiles, c, dec, grid,
                     stream, start, stop)
 }
 

@@ -209,10 +209,18 @@ def test_decoder_7b_list_stats_clip_skip_sequence():
             s.grad[local] = torch.tensor(vals[lo:hi], dtype=torch.bfloat16, device=DEV)
     launches = ra.radamw_launch_count()
     snap = [s.param[:4096].clone() for s in segs]
+
+    def bit_sums():  # every word of p, m and v, summed as integers
+        return [tuple(int(t.view(torch.int32).sum(dtype=torch.int64)) for t in (s.param, s.exp_avg, s.exp_avg_sq))
+                for s in segs]
+
+    sums = bit_sums()
     res, step = fused(step, 2)
     assert res.found_inf and res.nonfinite == k == 6738 and step == 1 and not res.updated
     assert all(bits_equal(a, s.param[:4096]) for a, s in zip(snap, segs))
-    assert ra.radamw_launch_count() > launches  # statistics ran; the update did not
+    # statistics ran and the update kernels queued behind them read the skip and wrote nothing
+    assert ra.radamw_launch_count() > launches
+    assert bit_sums() == sums
     # clean step at t = 2
     for i, s in enumerate(segs):
         s.grad.copy_(synth.stored_grad(s.grad.numel(), 1e-4, 1.0, "bf16", (0, "dec7b", i, "g3"), DEV))

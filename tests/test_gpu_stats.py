@@ -161,9 +161,12 @@ def _fused_case(sizes, gdt, inject, max_norm, key, step0=0, amsgrad=False, hiera
     if skip_ref:
         assert not res.updated and step == step0
         assert all(torch.equal(a, s.param) for a, s in zip(snap, segs))
-        # one analysis launch for the whole list, the merge levels, the final merge; no update
+        # one analysis launch for the whole list, the merge levels, the final merge, and the update
+        # launches queued behind it, which read the device's skip decision and write nothing
         extra = ra.radamw_stats_plan(sum(ra.radamw_grad_stats_rows(n, TORCH_GDT[gdt]) for n in sizes))[1]
-        assert nstats > 1 and launched == 1 + extra + 1
+        solo = sum(1 for n in sizes if n >= 1 << 22)
+        shared = sum(1 for n in sizes if 0 < n < 1 << 22)
+        assert nstats > 1 and launched == 1 + extra + 1 + solo + (1 if shared else 0)
     else:
         assert res.updated and step == step0 + 1
         for (p_ref, st_ref), s in zip(refs, segs):
@@ -213,4 +216,67 @@ def test_fused_statistics_launch_equals_per_tensor_launches(gdt):
     assert res.found_inf and not res.updated and step == 3
     assert res.nonfinite == c_ref == 4 and res.sumsq == s_ref
     extra = ra.radamw_stats_plan(rows)[1]
-    assert ra.radamw_launch_count() - before == 1 + extra + 1  # one analysis launch, merges, final merge
+    # one analysis launch, merges, final merge, and the queued updates (9,000,001 alone, the rest shared)
+    assert ra.radamw_launch_count() - before == 1 + extra + 1 + 2
+
+
+def _norm_of(grads, gdt, scale):
+    acc = oracle.StatsAccumulator()
+    for g in grads:
+        acc.add(grad_host(g), gdt)
+    return math.sqrt(acc.result[0]) / scale
+
+
+@pytest.mark.parametrize("gdt,scale,clip_at,maximize", [
+    ("f32", 1.0, None, False),      # no clipping
+    ("f32", 3.0, 0.5, False),       # clip active, non-power-of-two scale
+    ("bf16", 1000.0, 2.0, True),    # maximize: the device takes the sign from the launch
+    ("f16", 0.37, 1.0, False),      # scale below one
+    ("bf16", 1.0, "at", False),     # max_norm equal to the norm: clip within rounding of 1
+    ("f32", 7.0, 1e9, True),        # bound far above the norm: clip == 1
+])
+def test_device_decision_matches_host_decision(gdt, scale, clip_at, maximize):
+    """The fused step decides on the device (the final merge writes skip and
+    the clipped FP32 unscale factor; the queued update kernels read them);
+    the same step composed from separate calls decides on the host
+    (radamw_read_report + radamw_decide + radamw_step_multi).  Over five
+    steps, every output bit agrees."""
+    announce(f"device decision {gdt} scale={scale} clip={clip_at} max={maximize}")
+    key = (0, "devdec", gdt, str(scale), str(clip_at), maximize)
+    sizes = [3, 4096, 2049, 1_000_001, 5_000_000]
+    opts = ra.options(lr=1e-3, weight_decay=1e-2, maximize=maximize)
+    a, b = [], []
+    for i, n in enumerate(sizes):
+        p = synth.normal(n, 0.02, key + (i, "p")).to(DEV)
+        mk = lambda: torch.zeros(n, device=DEV)
+        a.append(ra.Segment(p, torch.empty(n, device=DEV, dtype=TORCH_GDT[gdt]), mk(), mk()))
+        b.append(ra.Segment(p.clone(), a[-1].grad, mk(), mk()))
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+    rows_total = sum(ra.radamw_grad_stats_rows(n, TORCH_GDT[gdt]) for n in sizes)
+    rows = torch.empty(3 * rows_total, dtype=torch.int32, device=DEV)
+    scratch = torch.empty(max(1, ra.radamw_stats_plan(rows_total)[0]), device=DEV)
+    report = torch.empty(3, dtype=torch.int32, device=DEV)
+    sa = sb = 0
+    for t in range(1, 6):
+        for i, s in enumerate(a):
+            s.grad.copy_(synth.stored_grad(sizes[i], 1e-3, scale, gdt, key + (i, "g", t)).to(DEV))
+        max_norm = clip_at
+        if clip_at == "at":
+            max_norm = _norm_of([s.grad for s in a], gdt, scale)
+        res, sa = ra.radamw_fused_step_multi(a, sa, opts, scale, max_norm, True, ws)
+        off = 0
+        for s in b:
+            off += ra.radamw_grad_stats(s.grad, rows, off)
+        ra.radamw_merge_stats(rows, rows_total, scratch, report, True)
+        host = ra.radamw_read_report(report)
+        ctrl, hres = ra.radamw_decide(host, scale, max_norm)
+        updated, sb = ra.radamw_step_multi(b, sb, opts, ctrl)
+        torch.cuda.synchronize()
+        assert (res.sumsq, res.nonfinite, res.clip_coef, res.total_norm) == \
+            (hres.sumsq, hres.nonfinite, hres.clip_coef, hres.total_norm)
+        assert res.updated and updated and sa == sb == t
+        if clip_at not in (None, 1e9):
+            assert res.clip_coef <= 1.0
+        for i, (x, y) in enumerate(zip(a, b)):
+            for u, w, what in ((x.param, y.param, "p"), (x.exp_avg, y.exp_avg, "m"), (x.exp_avg_sq, y.exp_avg_sq, "v")):
+                assert torch.equal(u.view(torch.int32), w.view(torch.int32)), f"step {t} tensor {i} {what}"

@@ -374,6 +374,7 @@ struct UpdateTable {
     size_t prefix_off = 0, coarse_off = 0;
     int32_t nseg = 0;
     int64_t tiles = 0;
+    bool copy = false;  // some segment writes a model copy
 };
 
 int build_update_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool first, UpdateTable *t) {
@@ -412,6 +413,7 @@ int build_update_table(std::vector<SegDesc> &segs, int gdt, bool amsgrad, bool f
     std::memcpy(t->bytes.data() + t->coarse_off, coarse.data(), coarse_bytes);
     t->nseg = nseg;
     t->tiles = tiles;
+    t->copy = std::any_of(segs.begin(), segs.end(), [](const SegDesc &d) { return d.model_kind != 0; });
     return RADAMW_OK;
 }
 
@@ -422,7 +424,7 @@ hipError_t launch_table_at(const UpdateTable &t, const char *base, int gdt, bool
     return launch_update_table(reinterpret_cast<const SegDesc *>(base),
                                reinterpret_cast<const int64_t *>(base + t.prefix_off),
                                reinterpret_cast<const int32_t *>(base + t.coarse_off), t.nseg, t.tiles, c, dec,
-                               gdt, amsgrad, first, update_grid(t.tiles), stream, ev_start, ev_stop);
+                               gdt, amsgrad, first, t.copy, update_grid(t.tiles), stream, ev_start, ev_stop);
 }
 
 // Several tensors in one launch, the table going through a staged slot

@@ -27,6 +27,55 @@ constexpr int UPDATE_UNROLL = RADAMW_UPDATE_UNROLL;
 constexpr int64_t UPDATE_TILE_CHUNKS = int64_t(UPDATE_BLOCK) * UPDATE_UNROLL;  // float4 chunks per tile
 constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 
+// Occupancy caps.  A CU of gfx950 has 160 KiB of LDS and holds up to 32
+// waves.  The streaming kernels use (almost) no LDS, so by default a CU
+// fills with 32 single-wave update workgroups, each with a whole tile of
+// every stream in flight.  That is more than HBM serves best: on MI355X
+// (2^28-element buckets, every update variant: FP32 / 16-bit gradients,
+// AdamW / AMSGrad, steady / first step, with and without a model copy)
+// throughput peaked when a CU held about 72 KiB of tile traffic (reads plus
+// writes), i.e. 8-16 workgroups, at 6.55-6.68 TB/s, against 6.0-6.3 TB/s at
+// full occupancy; fewer than that starved the memory system.  The cap is
+// applied by reserving LDS at launch that the kernels never touch.
+constexpr int64_t LDS_PER_CU = 160 * 1024;
+constexpr int MAX_WAVES_PER_CU = 32;
+constexpr int64_t UPDATE_CU_INFLIGHT_BYTES = 72 * 1024;
+
+// Dynamic LDS that, together with a kernel's `static_bytes` of static LDS,
+// lets exactly `cap` workgroups reside on one CU: the total is the largest
+// multiple of the 512-byte allocation unit not above LDS_PER_CU / cap, which
+// stays above LDS_PER_CU / (cap + 1) for every cap up to 17.
+inline size_t lds_for_cap(int64_t cap, size_t static_bytes) {
+    if (cap < 1) cap = 1;
+    const size_t total = static_cast<size_t>(LDS_PER_CU / cap) & ~size_t(511);
+    const size_t st = (static_bytes + 511) & ~size_t(511);
+    return total > st ? total - st : 0;
+}
+
+// HBM bytes one element of an update moves: p, the gradient and (after the
+// first step) m, v and v_max read; p, m, v, v_max and the optional 16-bit
+// model copy written.
+inline int64_t update_bytes_per_element(int gdt, bool amsgrad, bool first, bool copy) {
+    int64_t b = 4 + (gdt == 0 ? 4 : 2) + 12;  // read p, g; write p, m, v
+    if (!first) b += 8;                       // read m, v
+    if (amsgrad) b += first ? 4 : 8;          // [read] and write v_max
+    if (copy) b += 2;
+    return b;
+}
+
+// The LDS reservation of a streaming launch of single-wave workgroups with
+// no static LDS, each moving `bytes_per_element` per element of a
+// UPDATE_TILE_ELEMS tile: the largest number of resident workgroups whose
+// tiles stay within UPDATE_CU_INFLIGHT_BYTES.
+inline size_t stream_lds_reservation(int64_t bytes_per_element) {
+    const int64_t cap = UPDATE_CU_INFLIGHT_BYTES / (bytes_per_element * UPDATE_TILE_ELEMS);
+    return cap >= MAX_WAVES_PER_CU ? 0 : lds_for_cap(cap, 0);
+}
+
+inline size_t update_lds_reservation(int gdt, bool amsgrad, bool first, bool copy) {
+    return stream_lds_reservation(update_bytes_per_element(gdt, amsgrad, first, copy));
+}
+
 // Multi-tensor launch policy.  On MI355X, back-to-back launches of large
 // tensors pipeline with no visible gap, and a shared launch across large
 // tensors held in separate allocations measured 7-10% slower than one
@@ -57,6 +106,12 @@ constexpr int STATS_UNROLL = RADAMW_STATS_UNROLL;
 #define RADAMW_STATS_ROWS_CAP 8192
 #endif
 constexpr int64_t STATS_ROWS_CAP = RADAMW_STATS_ROWS_CAP;  // records per tensor, at most
+// FP32 analysis keeps 16 KiB in flight per workgroup (256 lanes x 4
+// chunks); on MI355X it read fastest with 4 resident workgroups per CU (7.1
+// against 6.9 TB/s at the full 8).  The 16-bit analysis spends more ALU per
+// byte (8 binary64 FMAs per 16-byte chunk) and needs every wave it can get
+// (capping it cost up to 35%), so it runs uncapped.
+constexpr int STATS_F32_WG_PER_CU = 4;
 constexpr int MERGE_BLOCK = 1024;            // merge workgroup = fan-in
 constexpr int64_t MERGE_FAN_IN = 1024;
 constexpr int64_t STATS_MAX_ROWS = 4194304;  // accepted by the merge plan
@@ -154,10 +209,11 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gl(T *p) {
 hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, const Decision *dec, int gdt,
                                 bool amsgrad, bool first, int grid, hipStream_t stream, hipEvent_t start,
                                 hipEvent_t stop);
+// copy: some segment of the table writes a model copy.
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
                                const Coefs &c, const Decision *dec, int gdt, bool amsgrad, bool first,
-                               int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                               bool copy, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 // One gradient of a multi-tensor statistics launch: its records are
 // out[row_begin, row_begin + rows), laid out exactly as a single-tensor
 // launch would write them.

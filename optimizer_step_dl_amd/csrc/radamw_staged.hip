@@ -162,25 +162,30 @@ static hipError_t staged_all(float *p, const void *g, float *m, float *v, float 
                              int64_t n, const Coefs &c, hipStream_t s, int *launched) {
     const int64_t lanes = (n >> 2) + (n & 3);
     const dim3 grid(static_cast<unsigned>((lanes + STAGED_BLOCK - 1) / STAGED_BLOCK)), block(STAGED_BLOCK);
+    // the fused kernels' occupancy rule, from each kernel's own streams
+    constexpr int64_t gb = GDT == G_F32 ? 4 : 2;
+    const size_t lds_moment = stream_lds_reservation(gb + (FIRST ? 4 : 8));  // g, [m or v], m or v
+    const size_t lds_vmax = stream_lds_reservation(FIRST ? 8 : 12);          // v, [vmax], vmax
+    const size_t lds_rest = stream_lds_reservation(12);                      // two reads, one write
     hipError_t e;
     *launched = 0;
-    hipLaunchKernelGGL((staged_m<GDT, FIRST>), grid, block, 0, s, g, m, n, c);
+    hipLaunchKernelGGL((staged_m<GDT, FIRST>), grid, block, lds_moment, s, g, m, n, c);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     ++*launched;
-    hipLaunchKernelGGL((staged_v<GDT, FIRST>), grid, block, 0, s, g, v, n, c);
+    hipLaunchKernelGGL((staged_v<GDT, FIRST>), grid, block, lds_moment, s, g, v, n, c);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     ++*launched;
     const float *vu = v;
     if (vmax) {
-        hipLaunchKernelGGL((staged_vmax<FIRST>), grid, block, 0, s, v, vmax, n);
+        hipLaunchKernelGGL((staged_vmax<FIRST>), grid, block, lds_vmax, s, v, vmax, n);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         ++*launched;
         vu = vmax;
     }
-    hipLaunchKernelGGL(staged_delta, grid, block, 0, s, m, vu, delta, n, c);
+    hipLaunchKernelGGL(staged_delta, grid, block, lds_rest, s, m, vu, delta, n, c);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     ++*launched;
-    hipLaunchKernelGGL(staged_param, grid, block, 0, s, p, delta, n, c);
+    hipLaunchKernelGGL(staged_param, grid, block, lds_rest, s, p, delta, n, c);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     ++*launched;
     return hipSuccess;

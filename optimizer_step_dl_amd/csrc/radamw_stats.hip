@@ -300,11 +300,21 @@ __global__ __launch_bounds__(MERGE_BLOCK) void stats_merge_decide(const StatsRec
     }
 }
 
+// Static LDS of an analysis workgroup (block_finish's per-wave partials).
+constexpr size_t ANALYZE_STATIC_LDS = (STATS_BLOCK / 64) * (sizeof(double) + sizeof(uint64_t));
+
+// The FP32 analysis runs capped at STATS_F32_WG_PER_CU resident workgroups
+// per CU; the 16-bit ones are uncapped.
+inline size_t analyze_lds_reservation(int gdt) {
+    return gdt == G_F32 ? lds_for_cap(STATS_F32_WG_PER_CU, ANALYZE_STATIC_LDS) : 0;
+}
+
 hipError_t launch_analyze(const void *g, int gdt, int64_t n, int32_t head, int64_t rows,
                           StatsRec *out, hipStream_t stream) {
     switch (gdt) {
     case G_F32:
-        hipLaunchKernelGGL(grad_analyze<G_F32>, dim3(rows), dim3(STATS_BLOCK), 0, stream, g, n, head, rows, out);
+        hipLaunchKernelGGL(grad_analyze<G_F32>, dim3(rows), dim3(STATS_BLOCK), analyze_lds_reservation(G_F32),
+                           stream, g, n, head, rows, out);
         break;
     case G_F16:
         hipLaunchKernelGGL(grad_analyze<G_F16>, dim3(rows), dim3(STATS_BLOCK), 0, stream, g, n, head, rows, out);
@@ -322,7 +332,10 @@ hipError_t launch_analyze_table(const StatsSeg *segs_dev, const int32_t *coarse_
                                 int gdt, StatsRec *out, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(total_rows)), block(STATS_BLOCK);
     switch (gdt) {
-    case G_F32: hipLaunchKernelGGL(grad_analyze_table<G_F32>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
+    case G_F32:
+        hipLaunchKernelGGL(grad_analyze_table<G_F32>, grid, block, analyze_lds_reservation(G_F32), stream, segs_dev,
+                           coarse_dev, out);
+        break;
     case G_F16: hipLaunchKernelGGL(grad_analyze_table<G_F16>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
     case G_BF16: hipLaunchKernelGGL(grad_analyze_table<G_BF16>, grid, block, 0, stream, segs_dev, coarse_dev, out); break;
     default: return hipErrorInvalidValue;

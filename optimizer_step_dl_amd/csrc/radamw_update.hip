@@ -18,8 +18,10 @@
 // any arithmetic, and the data is touched exactly once, so loads and stores
 // carry the nontemporal hint (measured: ~5% faster than default caching).
 // Each workgroup is a single wave64 that handles one tile and exits, so the
-// dispatcher keeps the whole chip full of short, independent request
-// streams.  No MFMA: there is no contraction here.
+// dispatcher keeps the whole chip busy with short, independent request
+// streams; an LDS reservation at launch caps how many of them a CU holds at
+// once, which HBM serves faster than a full CU.  No MFMA: there is no
+// contraction here.
 #include "radamw_math.h"
 
 #include <hip/hip_ext.h>
@@ -298,21 +300,21 @@ __global__ __launch_bounds__(UPDATE_BLOCK) void adamw_update_table(
     any_tile<GDT, AMS, FIRST>(seg, t - prefix[lo], c, dec);
 }
 
+// `lds` is the occupancy reservation (update_lds_reservation): dynamic LDS
+// the kernels never touch, which caps the workgroups resident on a CU.
 template <int GDT, bool AMS, bool FIRST>
 static hipError_t launch_single_t(const SegDesc &seg, const Coefs &c, const Decision *dec, int grid,
-                                  hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-    hipExtLaunchKernelGGL((adamw_update_single<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
+                                  size_t lds, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL((adamw_update_single<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), lds,
                           st, start, stop, 0, seg, c, dec);
     return hipGetLastError();
 }
 
 template <int GDT, bool AMS, bool FIRST>
 static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, const int32_t *coarse,
-                                 int32_t nseg, int64_t total, const Coefs &c, const Decision *dec, int grid,
-                                 hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-    (void)nseg;
-    (void)total;
-    hipExtLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), 0,
+                                 const Coefs &c, const Decision *dec, int grid, size_t lds, hipStream_t st,
+                                 hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL((adamw_update_table<GDT, AMS, FIRST>), dim3(grid), dim3(UPDATE_BLOCK), lds,
                           st, start, stop, 0, segs, prefix, coarse, c, dec);
     return hipGetLastError();
 }
@@ -337,15 +339,18 @@ static hipError_t launch_table_t(const SegDesc *segs, const int64_t *prefix, con
 hipError_t launch_update_single(const SegDesc &seg, const Coefs &c, const Decision *dec, int gdt,
                                 bool amsgrad, bool first, int grid, hipStream_t stream, hipEvent_t start,
                                 hipEvent_t stop) {
-    RADAMW_DISPATCH(launch_single_t, seg, c, dec, grid, stream, start, stop)
+    const size_t lds = update_lds_reservation(gdt, amsgrad, first, seg.model_kind != 0);
+    RADAMW_DISPATCH(launch_single_t, seg, c, dec, grid, lds, stream, start, stop)
 }
 
 hipError_t launch_update_table(const SegDesc *segs_dev, const int64_t *tile_prefix_dev,
                                const int32_t *coarse_dev, int32_t nseg, int64_t total_tiles,
                                const Coefs &c, const Decision *dec, int gdt, bool amsgrad, bool first,
-                               int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, nseg, total_tiles, c, dec, grid,
-                    stream, start, stop)
+                               bool copy, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    (void)nseg;
+    (void)total_tiles;
+    const size_t lds = update_lds_reservation(gdt, amsgrad, first, copy);
+    RADAMW_DISPATCH(launch_table_t, segs_dev, tile_prefix_dev, coarse_dev, c, dec, grid, lds, stream, start, stop)
 }
 
 }  // namespace radamw

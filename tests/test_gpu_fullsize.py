@@ -17,7 +17,7 @@ import torch
 import oracle
 import synth
 import optimizer_step_dl_amd as ra
-from gpu_helpers import DEV, announce, bits_equal, contract_one_step, grad_host, oracle_opts
+from gpu_helpers import DEV, announce, bits_equal, contract_one_step, grad_host, oracle_opts, ulps_of
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,9 @@ def _oracle_on_sample(p, g, m, v, vmax, step, opts, scale, gdt):
     ("amsgrad", "f32", "outofplace"), ("adamw", "bf16", "inplace")])
 def test_bucket_2pow28_steady_state(variant, gdt, mode):
     """The 268,435,456-element bucket at t = 1000 as bench.py builds it,
-    launched as bench.py launches it (one-segment radamw_step_multi in place,
-    radamw_step out of place); oracle on 67k sampled elements incl. both ends."""
+    updated the way bench.py's update-only variants launch it (one-segment
+    radamw_step_multi in place, radamw_step out of place); oracle on 67k
+    sampled elements incl. both ends."""
     n = 1 << 28
     announce(f"bucket 2^28 {variant} {gdt} {mode}")
     amsgrad = variant == "amsgrad"
@@ -86,6 +87,48 @@ def test_bucket_2pow28_steady_state(variant, gdt, mode):
         contract_one_step(after[3].numpy(), st_ref.max_exp_avg_sq, "vmax")
         assert bool(torch.all(outs[3] >= outs[2]))
     assert bool(torch.isfinite(outs[0]).all()) and bool(torch.isfinite(outs[1]).all())
+
+
+def test_bucket_2pow28_fused_step_as_benched():
+    """The headline step exactly as bench.py times it: one
+    radamw_fused_step_multi call over the one-segment 2^28 bucket (FP32
+    grads, AdamW, t = 1000) with hierarchical statistics and a clip at
+    max_grad_norm = 1.0 (the norm is ~16.4, so the clip is active).  The
+    report's count is the oracle's over all 2^28 gradients bit for bit and its
+    sum lies within the oracle's sequential FP64 bound; the clip coefficient
+    is the oracle's rule applied to the report, bit for bit; sampled elements
+    (both ends and 64k random) match the oracle run at the clipped scale."""
+    n = 1 << 28
+    announce("bucket 2^28 fused step as benched")
+    key = (0, "bucket", n)
+    p = synth.normal(n, 0.02, key + ("p",), DEV)
+    g = synth.stored_grad(n, 1e-3, 1.0, "f32", key + ("g",), DEV)
+    m, v, _ = synth.steady_state(n, key, False, DEV, m_std=1e-4, v_root_std=1e-3)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    seglist = ra.SegmentList([ra.Segment(p, g, m, v, None)])
+    ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=DEV)
+    idx_dev = torch.from_numpy(_sample_idx(n, 65536, (0, "bucket-fused-sample"))).to(DEV)
+    before = [_gather(t, idx_dev) for t in (p, g, m, v)]
+    sumsq, count = oracle.grad_stats(grad_host(g), "f32")
+    res, step = ra.radamw_fused_step_multi(seglist, 999, opts, 1.0, 1.0, True, ws)
+    torch.cuda.synchronize()
+    assert res.updated and not res.found_inf and step == 1000
+    assert res.nonfinite == count == 0
+    assert abs(res.sumsq - sumsq) <= (n - 1) * 2.0**-53 * sumsq
+    clip = oracle.clip_coefficient(res.sumsq, 1.0, 1.0)
+    assert res.clip_coef == clip and 0.0 < clip < 1.0
+    skip, eff = oracle.decide(res.sumsq, res.nonfinite, 1.0, 1.0)
+    assert not skip
+    p_ref, st_ref = _oracle_on_sample(*before, None, 999, opts, eff, "f32")
+    after = [_gather(t, idx_dev).numpy() for t in (p, m, v)]
+    contract_one_step(after[0], p_ref, "p")
+    contract_one_step(after[1], st_ref.exp_avg, "m")
+    contract_one_step(after[2], st_ref.exp_avg_sq, "v")
+    # the moments sit far below the absolute bar: bound them in ulps of the summed terms
+    g_unscaled = before[1].numpy().astype(np.float64) / eff
+    m_terms = np.abs(0.9 * before[2].numpy().astype(np.float64)) + np.abs(0.1 * g_unscaled)
+    ulps_of(after[1], st_ref.exp_avg, m_terms.astype(np.float32), 4, "m")
+    ulps_of(after[2], st_ref.exp_avg_sq, st_ref.exp_avg_sq, 8, "v")
 
 
 def _decoder_segments(shapes, gdt, scale, amsgrad, step, key, std):

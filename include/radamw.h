@@ -62,7 +62,9 @@ enum {
                                 the step count would overflow                 */
     RADAMW_ERR_ALIAS = -3,   /* a written range overlaps another range         */
     RADAMW_ERR_ALIGN = -4,   /* pointer not aligned to its element size        */
-    RADAMW_ERR_RANGE = -5,   /* row count / capacity / scratch size out of range */
+    RADAMW_ERR_RANGE = -5,   /* row count / capacity / scratch size out of
+                                range; an element count above 2^48 (any
+                                entry point taking n)                         */
     RADAMW_ERR_HIP = -6      /* a HIP runtime call failed (see
                                 radamw_last_hip_error)                         */
 };

@@ -129,6 +129,11 @@ bool valid_dtype(int gdt) { return gdt == RADAMW_F32 || gdt == RADAMW_F16 || gdt
 
 size_t grad_bytes(int gdt) { return gdt == RADAMW_F32 ? 4 : 2; }
 
+// Element counts above this are rejected (RADAMW_ERR_RANGE) before any byte
+// size is formed, so n * element size cannot overflow; any tensor that fits
+// in device memory is far below it.
+constexpr int64_t MAX_ELEMENTS = int64_t(1) << 48;
+
 // Pointer validation for one call.  A pointer must be device (or managed)
 // memory of the stream's device, aligned to its element size, and the bytes
 // the call touches must lie inside the allocation that holds it.  Each
@@ -536,6 +541,7 @@ int check_segments(const radamw_segment *segs, int32_t nseg, int gdt, bool amsgr
     for (int32_t i = 0; i < nseg; ++i) {
         const radamw_segment &s = segs[i];
         if (s.n < 0) return RADAMW_ERR_INVALID;
+        if (s.n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
         if (s.n == 0) continue;  // empty tensors may carry null pointers
         if ((s.max_exp_avg_sq != nullptr) != amsgrad) return RADAMW_ERR_STATE;
         ++active;
@@ -912,6 +918,7 @@ int radamw_step(const float *p, const void *g, radamw_dtype gdt, int64_t n, cons
     if ((rc = check_options(opts))) return rc;
     if ((rc = check_control(ctrl))) return rc;
     if (!valid_dtype(gdt) || n < 0 || !in || !out || !updated) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
     const bool ams = opts->amsgrad != 0;
     const bool first = in->step == 0;
     if (in->step == UINT64_MAX) return RADAMW_ERR_STATE;
@@ -959,6 +966,7 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n, ra
     if ((rc = check_options(opts))) return rc;
     if ((rc = check_control(ctrl))) return rc;
     if (!valid_dtype(gdt) || n < 0 || !st || !updated) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
     if (st->step == UINT64_MAX) return RADAMW_ERR_STATE;
     const bool ams = opts->amsgrad != 0;
     if (n == 0) {
@@ -985,6 +993,7 @@ int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_
     if ((rc = check_options(opts))) return rc;
     if ((rc = check_control(ctrl))) return rc;
     if (!valid_dtype(gdt) || n < 0 || !st || !updated) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
     if (st->step == UINT64_MAX) return RADAMW_ERR_STATE;
     const bool ams = opts->amsgrad != 0;
     if (n == 0) {
@@ -1082,6 +1091,7 @@ int radamw_stats_plan(int64_t rows, int64_t *scratch_elements, int32_t *extra_me
 
 int64_t radamw_grad_stats_rows(int64_t n, radamw_dtype gdt) {
     if (n < 0 || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
     return stats_rows(n, gdt);
 }
 
@@ -1089,6 +1099,7 @@ int radamw_grad_stats(const void *g, radamw_dtype gdt, int64_t n, radamw_stats *
                       int64_t rows_capacity, int64_t *rows_written, radamw_stream_t stream_) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     if (!valid_dtype(gdt) || n < 0 || !rows_written || rows_capacity < 0) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
     const int64_t rows = stats_rows(n, gdt);
     if (rows == 0) {
         *rows_written = 0;
@@ -1159,6 +1170,7 @@ int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg, r
     int64_t rows = 0;
     for (int32_t i = 0; i < nseg; ++i) {
         if (segs[i].n < 0) return RADAMW_ERR_INVALID;
+        if (segs[i].n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
         rows += stats_rows(segs[i].n, gdt);
     }
     if (rows == 0) return 0;
@@ -1264,8 +1276,10 @@ int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gd
     if (!list_out || nseg < 0 || (nseg > 0 && !segs) || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
     if (amsgrad != 0 && amsgrad != 1) return RADAMW_ERR_INVALID;
     if (models && model_dtype != RADAMW_F16 && model_dtype != RADAMW_BF16) return RADAMW_ERR_INVALID;
-    for (int32_t i = 0; i < nseg; ++i)
+    for (int32_t i = 0; i < nseg; ++i) {
         if (segs[i].n < 0) return RADAMW_ERR_INVALID;
+        if (segs[i].n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
+    }
     int rc, dev;
     if ((rc = stream_device(stream, &dev))) return rc;
     int64_t active = 0;

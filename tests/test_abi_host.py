@@ -162,6 +162,19 @@ def test_validation_before_any_device_call(lib):
     rc = lib.radamw_step_inplace(None, None, 0, 16, ctypes.byref(st), ctypes.byref(ams),
                                  ctypes.byref(ra.control()), None, ctypes.byref(upd))
     assert rc == -2
+    # element counts whose byte sizes could overflow: a range error, checked before any pointer
+    rc = lib.radamw_step_inplace(None, None, 0, 2**60, ctypes.byref(st), ctypes.byref(good),
+                                 ctypes.byref(ra.control()), None, ctypes.byref(upd))
+    assert rc == -5
+    st_out = _abi._State(0, None, None, None)
+    rc = lib.radamw_step(None, None, 0, 2**48 + 1, ctypes.byref(st), None, ctypes.byref(st_out), ctypes.byref(good),
+                         ctypes.byref(ra.control()), None, ctypes.byref(upd))
+    assert rc == -5 and st_out.step == 0
+    assert lib.radamw_grad_stats_rows(2**48 + 1, 0) == -5
+    assert lib.radamw_grad_stats_rows(2**48, 2) == 8192
+    huge = (_abi._Segment * 2)(_abi._Segment(None, None, None, None, None, 16),
+                               _abi._Segment(None, None, None, None, None, 2**62))
+    assert lib.radamw_fused_workspace_bytes(huge, 2, 0) == -5
     overflow = _abi._State(2**64 - 1, None, None, None)
     rc = lib.radamw_step_inplace(None, None, 0, 16, ctypes.byref(overflow), ctypes.byref(good),
                                  ctypes.byref(ra.control()), None, ctypes.byref(upd))

@@ -105,8 +105,8 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.stderr.write("bench.py: this build runs the optimizer step on one GPU only; "
-                         "--gpus above 1 is not supported (see the sharding design notes).\n")
+        sys.stderr.write("bench.py: the optimizer step is measured on one GPU only; --gpus above 1 is not "
+                         "supported (sharding the step over GPUs is designed, not implemented).\n")
         return 2
 
     import torch

@@ -36,7 +36,10 @@
  *     "增加的实际能力"); graph capture is not supported.
  *   - Thread safety: calls may come from several host threads; each call is
  *     independent apart from the launch counter and the per-device caches
- *     of the segment-table path, which are internally locked.
+ *     (segment-table staging, the mapped report page, the second update
+ *     stream), which are internally locked.  Multi-tensor calls on
+ *     different caller streams of one device share that device's second
+ *     stream, so their update launches may wait for one another.
  */
 #ifndef RADAMW_H
 #define RADAMW_H
@@ -214,9 +217,15 @@ int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_
  * flattened bucket is nseg == 1.  Launches: every tensor of at least 2^22
  * elements gets a launch of its own and all smaller tensors share a single
  * launch, so a list of many small tensors costs one launch, while large
- * tensors keep the single-tensor kernel (which MI355X pipelines back to
- * back without gaps, and which measured faster than sharing a launch).  All
- * launches use the same constants and the step count advances once.
+ * tensors keep the single-tensor kernel (which measured faster than sharing
+ * a launch).  All launches use the same constants and the step count
+ * advances once.  With two or more launches, every other one runs on a
+ * second stream the library keeps per device, so that the drain of one
+ * launch overlaps the start of the next: that stream first waits for all
+ * work queued on `stream` before the call, and `stream` waits for all of it
+ * before anything queued after the call, so the call still orders on
+ * `stream` exactly like a single launch.  The fused and list entry points
+ * below submit their update launches the same way.
  *   segs  : host array of nseg descriptors (device pointers inside).
  *   step  : host, the shared completed-step count; incremented on launch.
  * Segments with n == 0 are ignored; when every segment is empty nothing is

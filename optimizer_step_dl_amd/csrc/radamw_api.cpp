@@ -69,6 +69,14 @@ struct DeviceCache {
     // one merged record per list of a multi-list fused step (report_mu)
     StatsRec *group_rec = nullptr;
     int64_t group_cap = 0;
+    // a second stream for the update launches of a multi-tensor step
+    // (aux_mu): every other launch goes to it, so that one tensor's drain
+    // overlaps the next tensor's ramp; fork / join order it after the
+    // caller's earlier work and the caller's later work after it
+    std::mutex aux_mu;
+    hipStream_t aux = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t join = nullptr;
 };
 
 DeviceCache g_devices[MAX_DEVICES];
@@ -478,30 +486,80 @@ void split_launches(const std::vector<SegDesc> &active, std::vector<SegDesc> &so
     for (const SegDesc &d : active) (d.n >= MULTI_SOLO_MIN ? solo : shared).push_back(d);
 }
 
+// The device's auxiliary update stream and its two events (aux_mu held).
+int ensure_aux(DeviceCache &dc, int dev) {
+    if (dc.aux) return RADAMW_OK;
+    DeviceScope scope(dev);
+    hipStream_t s = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_status(e);
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(s);
+        return hip_status(e);
+    }
+    dc.aux = s;
+    dc.fork = f;
+    dc.join = j;
+    return RADAMW_OK;
+}
+
 // Submit the update launches of one step: every solo tensor, then the
 // shared ones in one launch, whose table is either staged now or already
 // resident in device memory (resident != null: its image and device base).
-// Measurement events, if requested, go on the first and the last launch.
+// With two or more launches, every other one goes to the device's auxiliary
+// stream: back-to-back launches on one stream each pay a ramp and a drain
+// (~3-4 us on MI355X), which two streams overlap.  The LDS reservation caps
+// residency per CU across both, so HBM sees the same bytes in flight.  The
+// auxiliary stream first waits for everything queued on `stream` so far
+// (the fused step's decision included), and `stream` waits for all of it
+// before anything queued after this call.  Measurement events, if
+// requested: the start on the first launch, the stop on `stream` after the
+// join.
 int submit_updates(const std::vector<SegDesc> &solo, std::vector<SegDesc> &shared, const UpdateTable *resident,
                    const char *resident_base, int gdt, bool ams, bool first, const Coefs &c, const Decision *dec,
                    int dev, hipStream_t stream, UpdateTiming timing) {
     const size_t launches = solo.size() + (shared.empty() ? 0 : 1);
-    size_t k = 0;
-    auto ev_start = [&]() { return k == 0 ? timing.start : nullptr; };
-    auto ev_stop = [&]() { return k + 1 == launches ? timing.stop : nullptr; };
+    DeviceCache &dc = g_devices[dev];
+    std::unique_lock<std::mutex> lock(dc.aux_mu, std::defer_lock);
+    const bool two = launches >= 2;
     int rc = RADAMW_OK;
+    if (two) {
+        lock.lock();
+        if ((rc = ensure_aux(dc, dev))) return rc;
+        hipError_t e = hipEventRecord(dc.fork, stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(dc.aux, dc.fork, 0);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    size_t k = 0;
+    auto on = [&]() { return two && (k & 1) ? dc.aux : stream; };
+    auto ev_start = [&]() { return k == 0 ? timing.start : nullptr; };
+    auto ev_stop = [&]() { return !two && k + 1 == launches ? timing.stop : nullptr; };
     for (const SegDesc &d : solo) {
-        if ((rc = launch_single(d, gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop()))) return rc;
+        if ((rc = launch_single(d, gdt, ams, first, c, dec, dev, on(), ev_start(), ev_stop()))) break;
         ++k;
     }
-    if (shared.size() == 1) {
-        rc = launch_single(shared[0], gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop());
-    } else if (shared.size() > 1 && resident) {
-        rc = hip_status(
-            launch_table_at(*resident, resident_base, gdt, ams, first, c, dec, stream, ev_start(), ev_stop()));
-        if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
-    } else if (shared.size() > 1) {
-        rc = launch_table(shared, gdt, ams, first, c, dec, dev, stream, ev_start(), ev_stop());
+    if (rc == RADAMW_OK) {
+        if (shared.size() == 1) {
+            rc = launch_single(shared[0], gdt, ams, first, c, dec, dev, on(), ev_start(), ev_stop());
+        } else if (shared.size() > 1 && resident) {
+            rc = hip_status(
+                launch_table_at(*resident, resident_base, gdt, ams, first, c, dec, on(), ev_start(), ev_stop()));
+            if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
+        } else if (shared.size() > 1) {
+            rc = launch_table(shared, gdt, ams, first, c, dec, dev, on(), ev_start(), ev_stop());
+        }
+    }
+    if (two) {
+        // join even after a failed launch, so that `stream` still orders
+        // after whatever reached the auxiliary stream
+        hipError_t e = hipEventRecord(dc.join, dc.aux);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, dc.join, 0);
+        if (e == hipSuccess && rc == RADAMW_OK && timing.stop) e = hipEventRecord(timing.stop, stream);
+        if (e != hipSuccess && rc == RADAMW_OK) rc = hip_status(e);
     }
     return rc;
 }

@@ -235,6 +235,45 @@ def test_multi_tensor_one_launch_matches_oracle_and_per_tensor(gdt, amsgrad):
         assert bits_equal(s.param, tw.param) and bits_equal(s.exp_avg_sq, tw.exp_avg_sq)
 
 
+@pytest.mark.parametrize("own_stream", [False, True])
+def test_multi_launches_are_ordered_on_the_callers_stream(own_stream):
+    """A list with several launches -- three tensors of at least 2^22
+    elements, each launched on its own, and small ones sharing a fourth
+    launch -- spreads its launches over the caller's stream and a second
+    stream of the library.  Work queued on the caller's stream right after
+    the call must see every update with no host synchronisation in between:
+    copies taken that way after each of three steps equal, bit for bit, the
+    copies taken after per-tensor launches on one stream."""
+    sizes = [1 << 22, 3, 5_000_001, 4097, (1 << 22) + 1, 2048]
+    announce(f"multi launch ordering own_stream={own_stream}")
+    opts = ra.options(lr=1e-3, weight_decay=0.01)
+    segs, _ = _make_segments(sizes, "f32", False, (0, "order"))
+    twins, _ = _make_segments(sizes, "f32", False, (0, "order"))
+    twin_states = [ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq) for s in twins]
+    grads = [[synth.normal(n, 1e-3, (0, "order", i, "g", t)) for i, n in enumerate(sizes)] for t in range(3)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if own_stream else torch.cuda.current_stream()
+    got, want = [], []
+    with torch.cuda.stream(stream):
+        step = 0
+        for t in range(3):
+            for s, tw, g in zip(segs, twins, grads[t]):
+                s.grad.copy_(g.to(DEV))
+                tw.grad.copy_(s.grad)
+            before = ra.radamw_launch_count()
+            updated, step = ra.radamw_step_multi(segs, step, opts, ra.control())
+            assert updated and step == t + 1
+            assert ra.radamw_launch_count() == before + 4
+            got.append([x.clone() for s in segs for x in (s.param, s.exp_avg, s.exp_avg_sq)])
+            for tw, ts in zip(twins, twin_states):
+                ra.radamw_step_inplace(tw.param, tw.grad, ts, opts, ra.control())
+            want.append([x.clone() for s in twins for x in (s.param, s.exp_avg, s.exp_avg_sq)])
+    torch.cuda.synchronize()
+    for t in range(3):
+        for k, (a, b) in enumerate(zip(got[t], want[t])):
+            assert bits_equal(a, b), f"step {t + 1}, array {k}"
+
+
 def test_multi_all_empty_launches_nothing():
     segs = [ra.Segment(torch.empty(0, device=DEV), torch.empty(0, device=DEV), torch.empty(0, device=DEV),
                        torch.empty(0, device=DEV))] * 3

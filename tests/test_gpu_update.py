@@ -274,6 +274,76 @@ def test_multi_launches_are_ordered_on_the_callers_stream(own_stream):
             assert bits_equal(a, b), f"step {t + 1}, array {k}"
 
 
+def _view(n, phase, dtype):
+    """An n-element view starting `phase` elements into its own buffer."""
+    return torch.zeros(n + 4, device=DEV, dtype=dtype)[phase:phase + n]
+
+
+@pytest.mark.parametrize("seed,gdt,amsgrad", [(0, "f32", False), (1, "f16", True), (2, "bf16", False),
+                                              (3, "f32", True), (4, "bf16", True), (5, "f16", False)])
+def test_random_lists_match_per_tensor_launches(seed, gdt, amsgrad):
+    """Seeded random tensor lists: 1-40 tensors, empty, tiny, mid-size and
+    >= 2^22-element ones (their own launches, so the launches alternate over
+    two streams), each array a view at a random element offset, mostly equal
+    across a tensor's arrays (aligned vector body after a scalar head) and
+    sometimes not (scalar path).  Two steps from no state (the first-step
+    variant, then the steady one) through one radamw_step_multi call equal
+    per-tensor radamw_step_inplace launches on contiguous twins bit for bit,
+    and tensors of up to 100k elements match the oracle per element."""
+    rng = np.random.Generator(np.random.PCG64(synth.derive_seed(0, "random-lists", seed)))
+    announce(f"random list seed={seed} {gdt} ams={amsgrad}")
+    scale = 1024.0 if gdt == "f16" else 1.0
+    sizes = []
+    for _ in range(int(rng.integers(1, 41))):
+        r = rng.random()
+        if r < 0.1:
+            sizes.append(0)
+        elif r < 0.25:
+            sizes.append(int(rng.integers(1, 17)))
+        elif r < 0.88:
+            sizes.append(int(np.exp(rng.uniform(np.log(17), np.log(400_000)))))
+        else:
+            sizes.append(int(rng.integers(1 << 22, (1 << 22) + 300_000)))
+    opts = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=amsgrad)
+    segs, twins, twin_states, refs = [], [], [], []
+    for i, n in enumerate(sizes):
+        phases = [int(rng.integers(0, 4))] * 5 if rng.random() < 0.7 else [int(x) for x in rng.integers(0, 4, 5)]
+        p0 = synth.normal(n, 0.02, (0, "rl", seed, i, "p"))
+        p, m, v = _view(n, phases[0], torch.float32), _view(n, phases[2], torch.float32), _view(n, phases[3], torch.float32)
+        x = _view(n, phases[4], torch.float32) if amsgrad else None
+        p.copy_(p0.to(DEV))
+        segs.append(ra.Segment(p, _view(n, phases[1], TORCH_GDT[gdt]), m, v, x))
+        st = new_gpu_state(n, amsgrad)
+        twins.append(ra.Segment(p0.to(DEV), torch.empty(n, device=DEV, dtype=TORCH_GDT[gdt]), st.exp_avg,
+                                st.exp_avg_sq, st.max_exp_avg_sq))
+        twin_states.append(ra.AdamWState(0, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq))
+        refs.append((p0.numpy().copy(), oracle.State(n, amsgrad)) if n <= 100_000 else None)
+    step = 0
+    for t in (1, 2):
+        for i, (s, tw) in enumerate(zip(segs, twins)):
+            g = synth.stored_grad(sizes[i], 1e-4 if gdt == "f16" else 1e-3, scale, gdt, (0, "rl", seed, i, "g", t))
+            s.grad.copy_(g.to(DEV))
+            tw.grad.copy_(s.grad)
+            if refs[i] is not None and sizes[i]:
+                oracle.adamw_step(refs[i][0], grad_host(g), gdt, refs[i][1], oracle_opts(opts), scale)
+        updated, step = ra.radamw_step_multi(segs, step, opts, ra.control(scale))
+        assert updated == any(sizes) and step == (t if any(sizes) else 0)
+        for tw, ts in zip(twins, twin_states):
+            ra.radamw_step_inplace(tw.param, tw.grad, ts, opts, ra.control(scale))
+    torch.cuda.synchronize()
+    for i, (s, tw) in enumerate(zip(segs, twins)):
+        if sizes[i] == 0:
+            continue
+        what = f"tensor {i} n={sizes[i]}"
+        for a, b in ((s.param, tw.param), (s.exp_avg, tw.exp_avg), (s.exp_avg_sq, tw.exp_avg_sq)):
+            assert bits_equal(a.contiguous(), b), what
+        if amsgrad:
+            assert bits_equal(s.max_exp_avg_sq.contiguous(), tw.max_exp_avg_sq), what
+        if refs[i] is not None:
+            st = ra.AdamWState(step, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)
+            _compare_state(s.param, st, refs[i][0], refs[i][1], amsgrad, what, one_step=True)
+
+
 def test_multi_all_empty_launches_nothing():
     segs = [ra.Segment(torch.empty(0, device=DEV), torch.empty(0, device=DEV), torch.empty(0, device=DEV),
                        torch.empty(0, device=DEV))] * 3

@@ -330,9 +330,11 @@ def bench_staged(torch, synth, ra, dev, stream, n):
     through a delta buffer; 48 / 60 B per parameter in the pages' model).
     (1) Device time per step on the 2^28 bucket, back-to-back launches.
     (2) The pages' A/B shape: 65,536 elements, BF16 grads, AMSGrad, 20
-    iterations per sample x 7 samples, both variants started from the same
-    materialised state, order alternated per sample, synchronised before and
-    after every batch, wall-clock ms per step (median / min / max)."""
+    iterations per sample x 7 samples, every arm started from the same
+    materialised state, order reversed every other sample, synchronised
+    before and after every batch, wall-clock ms per step (median / min /
+    max).  Arms: fused in place, staged, and fused out of place with its
+    outputs allocated every step (the pages' out-of-place API allocates)."""
     out = {}
     for variant, bpp_f, bpp_s in (("adamw", 28, 48), ("amsgrad", 36, 60)):
         amsgrad = variant == "amsgrad"
@@ -372,8 +374,9 @@ def bench_staged(torch, synth, ra, dev, stream, n):
     m0, v0, x0 = synth.steady_state(small, key, True, dev)
     o = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=True)
     c = ra.control(128.0)
+    names = ("fused", "staged", "fused_out_of_place")
     arms = {}
-    for name in ("fused", "staged"):
+    for name in names:
         arms[name] = [p0.clone(), m0.clone(), v0.clone(), x0.clone(), torch.empty_like(p0)]
 
     def run(name, k):
@@ -381,8 +384,13 @@ def bench_staged(torch, synth, ra, dev, stream, n):
         st = ra.AdamWState(10 + k, m, v, x)
         if name == "fused":
             ra.radamw_step_inplace(p, g, st, o, c)
-        else:
+        elif name == "staged":
             ra.radamw_step_staged_inplace(p, g, st, d, o, c)
+        else:
+            # the pages' out-of-place form: fresh outputs allocated every step
+            out = [torch.empty_like(p), torch.empty_like(m), torch.empty_like(v), torch.empty_like(x)]
+            ra.radamw_step(p, g, st, o, c, out[0], ra.AdamWState(0, out[1], out[2], out[3]))
+            arms[name][:4] = out
 
     for name in arms:  # warm both
         for k in range(5):
@@ -391,9 +399,9 @@ def bench_staged(torch, synth, ra, dev, stream, n):
         for dst, src in zip(arms[name][:4], (p0, m0, v0, x0)):
             dst.copy_(src)
     torch.cuda.synchronize()
-    samples = {"fused": [], "staged": []}
+    samples = {name: [] for name in names}
     for sample in range(7):
-        order = ("fused", "staged") if sample % 2 == 0 else ("staged", "fused")
+        order = names if sample % 2 == 0 else names[::-1]
         for name in order:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
@@ -401,14 +409,16 @@ def bench_staged(torch, synth, ra, dev, stream, n):
                 run(name, 20 * sample + k)
             torch.cuda.synchronize()
             samples[name].append((time.perf_counter() - t0) * 1e3 / 20)
-    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(arms["fused"][:4], arms["staged"][:4]))
+    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+               for other in ("staged", "fused_out_of_place") for a, b in zip(arms["fused"][:4], arms[other][:4]))
     shape = {"elements": small, "grad_dtype": "bf16", "amsgrad": True, "iterations": 20, "samples": 7,
              "states_bit_identical": bool(same)}
     for name, xs in samples.items():
         xs = sorted(xs)
         shape[name] = {"wall_ms_per_step_median": xs[len(xs) // 2], "min": xs[0], "max": xs[-1]}
     log(f"A/B 65,536 bf16 AMSGrad wall ms/step: fused {shape['fused']['wall_ms_per_step_median']:.4f}, staged "
-        f"{shape['staged']['wall_ms_per_step_median']:.4f}, identical states: {same}")
+        f"{shape['staged']['wall_ms_per_step_median']:.4f}, fused out of place with allocation "
+        f"{shape['fused_out_of_place']['wall_ms_per_step_median']:.4f}, identical states: {same}")
     out["pages_ab_shape_65536_bf16_amsgrad"] = shape
     return out
 

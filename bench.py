@@ -122,6 +122,7 @@ def main(argv=None):
     n = args.n
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs, n={n}")
+    smi_before = smi_snapshot()
 
     # ---------------------------------------------------- headline step --
     p, g, m, v, _ = build_inputs(torch, synth, n, "adamw", "f32", dev)
@@ -319,7 +320,8 @@ def main(argv=None):
         "decoder_7b_fused_step": decoder7,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip,
-                   "memory_bytes": props.total_memory, "clocks": clocks()},
+                   "memory_bytes": props.total_memory, "rocm_smi_before": smi_before,
+                   "rocm_smi_after": smi_snapshot()},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -400,6 +402,7 @@ def bench_staged(torch, synth, ra, dev, stream, n):
             dst.copy_(src)
     torch.cuda.synchronize()
     samples = {name: [] for name in names}
+    same = True
     for sample in range(7):
         order = names if sample % 2 == 0 else names[::-1]
         for name in order:
@@ -409,10 +412,13 @@ def bench_staged(torch, synth, ra, dev, stream, n):
                 run(name, 20 * sample + k)
             torch.cuda.synchronize()
             samples[name].append((time.perf_counter() - t0) * 1e3 / 20)
-    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
-               for other in ("staged", "fused_out_of_place") for a, b in zip(arms["fused"][:4], arms[other][:4]))
+        # every arm has now run the same iterations: parameters and moments
+        # must agree bit for bit after every measured batch
+        same = same and all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+                            for other in ("staged", "fused_out_of_place")
+                            for a, b in zip(arms["fused"][:4], arms[other][:4]))
     shape = {"elements": small, "grad_dtype": "bf16", "amsgrad": True, "iterations": 20, "samples": 7,
-             "states_bit_identical": bool(same)}
+             "states_bit_identical_after_every_batch": bool(same)}
     for name, xs in samples.items():
         xs = sorted(xs)
         shape[name] = {"wall_ms_per_step_median": xs[len(xs) // 2], "min": xs[0], "max": xs[-1]}
@@ -605,15 +611,22 @@ def cpu_baseline_threads(torch, synth, seconds):
                       f"into {cores} contiguous slices (one thread each), {steps} steps in {el:.1f} s"}
 
 
-def clocks():
-    """GPU clock levels as rocm-smi reports them (best effort; None if the
-    tool is missing or says nothing)."""
+def smi_snapshot():
+    """Clocks, power, DPM performance level, temperature, GPU and memory use
+    and driver version as rocm-smi reports them (best effort; None if the
+    tool is missing or says nothing).  Taken before and after the timed work,
+    so that the record shows the settings and any other load on the GPU."""
     import subprocess
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showperflevel", "--showtemp",
+                              "--showuse", "--showmemuse", "--showdriverversion", "--json"],
+                             capture_output=True, text=True, timeout=30)
         data = json.loads(out.stdout)
-        card = next(iter(data.values()))
-        return {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk"))}
+        snap = {}
+        for name, fields in data.items():
+            if isinstance(fields, dict):
+                snap.update({k.strip(): v for k, v in fields.items()})
+        return snap or None
     except Exception:
         return None
 

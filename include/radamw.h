@@ -487,9 +487,11 @@ uint64_t radamw_launch_count(void);
  * Measurement hook (not part of the method): the next radamw_step,
  * radamw_step_inplace, radamw_step_multi, radamw_fused_step_multi or list
  * step call on this thread that launches an update records start_event
- * when its first update kernel starts and stop_event when its last update
- * kernel ends (hipExtLaunchKernelGGL), so the host's submission latency is
- * not timed.
+ * when its first update kernel starts (hipExtLaunchKernelGGL), so the
+ * host's submission latency is not timed, and stop_event when its update
+ * kernels have ended: at the end of a single launch, or, when the launches
+ * are spread over two streams, on the caller's stream right after it has
+ * joined the second one.
  * The events are caller-created hipEvent_t of the stream's device; passing
  * NULL, NULL clears the request.  Always returns RADAMW_OK.
  */

@@ -280,3 +280,42 @@ def test_host_coefficients_at_late_steps(lib, betas):
             ibc2 = np.float32(float(1 / bc2))
         for got, want in ((np.float32(c[6]), step), (np.float32(c[7]), ibc2)):
             assert abs(int(got.view(np.int32)) - int(want.view(np.int32))) <= 1, (t, got, want)
+
+
+def test_plain_c_consumer(lib, tmp_path):
+    """include/radamw.h compiles as strict C99 (gcc -std=c99 -pedantic
+    -Werror), libradamw.so links from C, and the entry points that need no
+    device answer from C as through the binding: the pages' defaults and
+    merge-plan figures, the oracle's FP32 coefficients, the empty-call and
+    bad-scale contracts, and no launch."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(ROOT, "tests", "c_abi", "radamw_c_consumer.c")
+    exe = str(tmp_path / "radamw_c_consumer")
+    libdir = os.path.dirname(ra.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-L", libdir, "-l:libradamw.so", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, check=True, timeout=60).stdout
+    vals = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    gold = load_golden("defaults.json")
+    assert float(vals["beta1"]) == gold["beta1"] and float(vals["beta2"]) == gold["beta2"]
+    assert float(vals["eps"]) == gold["eps"] and float(vals["weight_decay"]) == gold["weight_decay"]
+    assert float(vals["lr"]) == gold["example_lr"] and vals["amsgrad"] == "0" and vals["maximize"] == "0"
+    plan = load_golden("stats_plan.json")
+    assert vals["plan_rc"] == "0"
+    assert int(vals["plan_scratch_elements"]) * 4 == plan["max_scratch_bytes"]
+    assert int(vals["plan_extra_merge_kernels"]) == plan["max_extra_merge_kernels"]
+    assert int(vals["plan_out_of_range"]) == -5
+    assert vals["coef_rc"] == "0"
+    c = [np.float32(float(vals[f"coef{i}"])) for i in range(9)]
+    o = oracle.coefficients(oracle.Options(), 1000)
+    assert (c[0], c[1], c[2], c[3]) == (o["beta1"], o["one_minus_beta1"], o["beta2"], o["one_minus_beta2"])
+    assert c[5] == o["decay"] and c[8] == o["eps"] and c[4] == np.float32(1 / 128)
+    py = ra.radamw_host_coefficients(ra.options(), 1000, 128.0)
+    assert c[6] == np.float32(py[6]) and c[7] == np.float32(py[7])
+    assert (vals["empty_rc"], vals["empty_updated"], vals["empty_step"]) == ("0", "0", "7")
+    assert vals["bad_scale_rc"] == "-1" and vals["status_alias"] == "overlapping buffers"
+    assert vals["launches"] == "0"

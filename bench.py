@@ -56,10 +56,15 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the update kernel's sources with comments and whitespace
+    removed: an edit of code (or of a macro) changes it, a comment does not."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

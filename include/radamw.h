@@ -329,9 +329,10 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale,
  * fused_step path of TR-zh: statistics of every active gradient ->
  * (hierarchical) merge -> 12-byte report read back -> skip or clip decision
  * -> the in-place update of radamw_step_multi.
- *   workspace : device, >= radamw_fused_workspace_bytes(...) bytes, 4-byte
- *               aligned, caller-owned: the rows, the merge scratch and a
- *               12-byte decision slot (its last 12 bytes).
+ *   workspace : device, >= radamw_fused_workspace_bytes(...) bytes, 8-byte
+ *               aligned (RADAMW_ERR_ALIGN otherwise), caller-owned: the
+ *               rows, the merge scratch and a decision slot in its last 12
+ *               bytes (an 8-byte record at an 8-byte boundary).
  *   max_grad_norm <= 0 disables clipping.
  *   result    : host struct, always filled on RADAMW_OK.
  * The final merge writes the report into host memory the library maps for

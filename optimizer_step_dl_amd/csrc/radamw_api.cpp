@@ -1263,7 +1263,7 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     if (workspace_bytes < need) return RADAMW_ERR_RANGE;
     {
         PtrChecker pc(dev);
-        if ((rc = pc.check(workspace, 4, need))) return rc;
+        if ((rc = pc.check(workspace, 8, need))) return rc;
     }
     {
         // the workspace is written; it may overlap no tensor of the step
@@ -1303,7 +1303,9 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     }
     // the update launches are queued behind the final merge and read its
     // decision from the workspace's last 12 bytes
-    Decision *dec_dev = reinterpret_cast<Decision *>(static_cast<char *>(workspace) + need - 12);
+    // the 8-byte decision, 8-byte aligned inside the workspace's last 12 bytes
+    const int64_t dec_off = (need - 12) % 8 == 0 ? need - 12 : need - 8;
+    Decision *dec_dev = reinterpret_cast<Decision *>(static_cast<char *>(workspace) + dec_off);
     std::vector<SegDesc> solo, shared;
     split_launches(inplace_descs(segs, nseg, nullptr, 0), solo, shared);
     const Coefs c = make_coefs(*opts, *step + 1, gradient_scale);

@@ -188,6 +188,25 @@ def test_fused_step_without_clip_is_plain_update():
     assert res.clip_coef == 1.0
 
 
+def test_fused_step_decision_slot_with_odd_rows_and_workspace_alignment():
+    """Three statistics rows (36 bytes): the decision moves to the last 8
+    bytes of the workspace to stay 8-byte aligned, and the clipped step
+    still matches the oracle.  A workspace that is only 4-byte aligned is
+    rejected (RADAMW_ERR_ALIGN) before anything is launched."""
+    announce("fused odd rows / workspace alignment")
+    res = _fused_case([4096, 8192], "f32", 0, 1e-3, (0, "fodd"))
+    assert res.clip_coef < 1.0
+    segs = [ra.Segment(torch.zeros(n, device=DEV), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                       torch.zeros(n, device=DEV)) for n in (4096, 8192)]
+    need = ra.radamw_fused_workspace_bytes(segs)
+    assert need == 3 * 12 + 12
+    ws = torch.zeros(need + 16, dtype=torch.uint8, device=DEV)
+    before = ra.radamw_launch_count()
+    with pytest.raises(ra.RadamwError) as e:
+        ra.radamw_fused_step_multi(segs, 5, ra.options(), 1.0, 1.0, True, ws[4:4 + need])
+    assert e.value.status == -4 and ra.radamw_launch_count() == before
+
+
 def test_fused_step_found_inf_skips_everything():
     announce("fused found_inf")
     res = _fused_case([4096, 1_000_000, 2049], "bf16", 3, 1.0, (0, "fi"), step0=4)

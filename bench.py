@@ -192,7 +192,7 @@ def main(argv=None):
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
          "adamw_f32_firststep", "adamw_f32_bf16copy"] if args.variants == "all" else
-        [v for v in args.variants.split(",") if v not in ("decoder_1b", "decoder_7b", "staged")])
+        [v for v in args.variants.split(",") if v not in ("decoder_1b", "decoder_7b", "staged", "optim_1b")])
     variants = {}
     for name in wanted:
         variant, gdt, mode = name.split("_")
@@ -263,6 +263,11 @@ def main(argv=None):
     if args.variants == "all" or "decoder_7b" in args.variants.split(","):
         decoder7 = bench_decoder_7b(torch, synth, ra, dev, stream)
 
+    # ------------- the torch optimizer over the 1.1B decoder's parameters --
+    optim_1b = None
+    if args.variants == "all" or "optim_1b" in args.variants.split(","):
+        optim_1b = bench_optimizer_1b(torch, synth, ra, dev, stream)
+
     # A plain elementwise copy of known size (1 GiB read, 1 GiB written):
     # torch's unary negation kernel.  It is the calibration kernel for the
     # rocprofv3 HBM counters and, timed, a context ceiling for streaming.
@@ -323,6 +328,7 @@ def main(argv=None):
         "decoder_1b_list": decoder,
         "staged_vs_fused": staged,
         "decoder_7b_fused_step": decoder7,
+        "fusedadamw_1b": optim_1b,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip,
                    "memory_bytes": props.total_memory, "rocm_smi_before": smi_before,
@@ -491,6 +497,58 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
         f"({out['update_gbs']:.0f} GB/s), stats + read-back {ms - ums:.2f} ms; per call {ms_call:.2f} ms; "
         f"clip {res.clip_coef:.4f}")
     del seglist, segs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_optimizer_1b(torch, synth, ra, dev, stream):
+    """FusedAdamW.step() -- the torch optimizer over the C ABI -- on the 201
+    parameters of the 1.1B decoder shapes, BF16 gradients N(0,1e-4), AdamW,
+    fused_step=True, max_grad_norm=1.0, hierarchical statistics: statistics,
+    merge, read-back, decision and update through one persistent tensor list
+    per launch bucket.  Wall-clock ms per step between synchronisations,
+    next to the C call alone on the same lists (radamw_lists_fused_step)."""
+    from optimizer_step_dl_amd.optim import FusedAdamW
+    shapes = synth.decoder_1b_shapes()
+    n_total = synth.total(shapes)
+    params = []
+    for i, (_, n) in enumerate(shapes):
+        key = (0, "optim-1b", i)
+        p = torch.nn.Parameter(synth.normal(n, 0.02, key + ("p",), dev))
+        if hasattr(p, "grad_dtype"):
+            p.grad_dtype = torch.bfloat16  # a BF16 .grad on an FP32 master parameter
+        p.grad = synth.stored_grad(n, 1e-4, 1.0, "bf16", key + ("g",), dev)
+        params.append(p)
+    opt = FusedAdamW(params, lr=1e-3, weight_decay=1e-4, fused_step=True, max_grad_norm=1.0,
+                     hierarchical_stats=True)
+    for _ in range(3):
+        opt.step()
+    torch.cuda.synchronize()
+    steps = 20
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        opt.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the same work as one C call per step on the optimizer's own lists
+    lists = list(opt._cache.values())
+    tlists = [lst for _, lst in lists]
+    group = opt.param_groups[0]
+    st = [opt.state[params[0]]["step"]] * len(tlists)
+    o = [opt._options(group)] * len(tlists)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        _, st = ra.radamw_lists_fused_step(tlists, st, o, 1.0, 1.0, True)
+    torch.cuda.synchronize()
+    c_ms = (time.perf_counter() - t0) * 1e3 / steps
+    res = opt.last_result
+    out = {"tensors": len(shapes), "n_params": n_total, "grad_dtype": "bf16", "launch_buckets": len(tlists),
+           "step_ms": ms, "params_per_s": n_total / (ms * 1e-3), "c_call_ms": c_ms,
+           "python_overhead_ms": ms - c_ms, "clip_coef": res.clip_coef if res else None}
+    log(f"FusedAdamW 1.1B fused step: {ms:.3f} ms ({out['params_per_s']:.3g} params/s), the C call alone "
+        f"{c_ms:.3f} ms, {len(tlists)} launch bucket(s)")
+    del opt, params, lists, tlists
     torch.cuda.empty_cache()
     return out
 

@@ -31,7 +31,9 @@ storage, and a fused step is one radamw_lists_fused_step call over all of
 them.  A cached list holds references to the tensors it was built from
 (including the gradients of the last step) until it is rebuilt or freed.
 Parameters must be FP32 device tensors; gradients FP32, FP16 or BF16 of the
-same shape.
+same shape.  Torch versions that check a gradient's dtype against its
+parameter's need ``param.grad_dtype`` set (to the 16-bit dtype, or None)
+before a 16-bit ``.grad`` is assigned to an FP32 master parameter.
 """
 from __future__ import annotations
 

@@ -109,6 +109,43 @@ def test_fused_step_clip_and_skip(hierarchical):
             assert opt.state[p]["step"] == mirror.st[i].step == steps_before[i] + (0 if skip else 1)
 
 
+@pytest.mark.parametrize("gdt", ["bf16", "f16"])
+def test_sixteen_bit_gradients_on_fp32_masters(gdt):
+    """FP32 master parameters with 16-bit .grad tensors (the parameter's
+    grad_dtype set where torch checks it), loss scale 1024, fused step with
+    clipping: each step matches the oracle run on the same stored gradients
+    with the same clip decision."""
+    announce(f"FusedAdamW {gdt} grads")
+    params = _model((0, "opt16", gdt))
+    ref = [host(p) for p in params]
+    states = [oracle.State(p.numel(), False) for p in params]
+    oo = oracle.Options(lr=1e-3, weight_decay=0.01)
+    opt = FusedAdamW(params, lr=1e-3, weight_decay=0.01, fused_step=True, max_grad_norm=0.05)
+    scale = 1024.0
+    for t in range(1, 4):
+        grads = []
+        for i, p in enumerate(params):
+            g = synth.stored_grad(p.numel(), 1e-3, scale, gdt, (0, "opt16", gdt, i, "g", t)).to(DEV)
+            if hasattr(p, "grad_dtype"):
+                p.grad_dtype = g.dtype
+            p.grad = g
+            grads.append(grad_host(g))
+        opt.step(gradient_scale=scale)
+        torch.cuda.synchronize()
+        res = opt.last_result
+        acc = oracle.StatsAccumulator()
+        for g in grads:
+            acc.add(g, gdt)
+        sumsq, count = acc.result
+        skip, eff = oracle.decide(res.sumsq, count, scale, 0.05)
+        assert res.nonfinite == count == 0 and not skip and res.clip_coef < 1.0
+        assert abs(res.sumsq - sumsq) <= (sum(SIZES) - 1) * 2.0**-53 * sumsq  # the oracle's sequential bound
+        for i, g in enumerate(grads):
+            oracle.adamw_step(ref[i], g, gdt, states[i], oo, eff)
+            contract_one_step(host(params[i]), ref[i], f"{gdt} param {i} step {t}")
+        assert all(opt.state[p]["step"] == t for p in params)
+
+
 def test_state_dict_resume_is_bit_exact():
     announce("FusedAdamW resume")
     pa = _model((0, "optr"))

@@ -1,12 +1,14 @@
 """Full-size GPU parity: the 2^28 bucket, the 1.1B-parameter 201-tensor list
-and the 6.7B-parameter 291-tensor list with statistics, clipping and an
-injected non-finite step.
+(as separate tensors and as one flattened bucket), the 6.7B-parameter
+291-tensor list with statistics, clipping and an injected non-finite step,
+and one tensor beyond 32-bit indexing.
 
-At these sizes the oracle checks sampled elements one by one (inputs gathered
-before the step, outputs gathered after it) and, for the statistics, every
-element (streamed tensor by tensor through the C oracle).  Whole-array
-properties (finiteness, AMSGrad max, bit-identity between launch forms) are
-checked on the device.
+Every element of every output is compared with the oracle: each tensor's
+pre-step state is kept on the device, staged through pinned host memory,
+updated there by the C oracle (threads over contiguous slices), and the GPU's
+result is compared with it on the device (gpu_helpers.compare_one_step_full:
+the 1e-6 (1 + |ref|) contract on p, m, v, v_max and ulp bars on the
+moments).  Statistics are checked over every gradient element.
 
 Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGrad",
 TR-zh = "训练与状态保存"."""
@@ -17,33 +19,20 @@ import torch
 import oracle
 import synth
 import optimizer_step_dl_amd as ra
-from gpu_helpers import DEV, announce, bits_equal, contract_one_step, grad_host, oracle_opts, ulps_of
+from gpu_helpers import (DEV, PinnedStage, announce, bits_equal, compare_one_step_full, grad_host,
+                         oracle_one_step_pinned, oracle_opts)
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample_idx(n, k, key):
-    rng = np.random.Generator(np.random.PCG64(synth.derive_seed(*key)))
-    idx = np.concatenate([np.arange(min(n, 1024)), np.arange(max(0, n - 1024), n), rng.integers(0, n, size=k)])
-    return np.unique(idx)
+def _bit_sum(t):
+    """Sum of a tensor's 32-bit words as integers: an exact fingerprint of
+    whether any word changed (up to a collision no bug produces)."""
+    return int(t.view(torch.int32).sum(dtype=torch.int64))
 
 
-def _gather(t, idx_dev):
-    return None if t is None else t.index_select(0, idx_dev).cpu()
-
-
-def _oracle_on_sample(p, g, m, v, vmax, step, opts, scale, gdt):
-    """Run the oracle on gathered host copies; returns (p, state)."""
-    pp = p.numpy().copy()
-    st = oracle.State(pp.size, vmax is not None)
-    st.step = step
-    if step > 0:
-        st.exp_avg = m.numpy().copy()
-        st.exp_avg_sq = v.numpy().copy()
-        if vmax is not None:
-            st.max_exp_avg_sq = vmax.numpy().copy()
-    oracle.adamw_step(pp, synth.grad_numpy(g), gdt, st, oracle_opts(opts), scale)
-    return pp, st
+def _clone(ts):
+    return [None if t is None else t.clone() for t in ts]
 
 
 @pytest.mark.parametrize("variant,gdt,mode", [
@@ -52,8 +41,8 @@ def _oracle_on_sample(p, g, m, v, vmax, step, opts, scale, gdt):
 def test_bucket_2pow28_steady_state(variant, gdt, mode):
     """The 268,435,456-element bucket at t = 1000 as bench.py builds it,
     updated the way bench.py's update-only variants launch it (one-segment
-    radamw_step_multi in place, radamw_step out of place); oracle on 67k
-    sampled elements incl. both ends."""
+    radamw_step_multi in place, radamw_step out of place); every element of
+    p, m, v (and v_max) against the oracle."""
     n = 1 << 28
     announce(f"bucket 2^28 {variant} {gdt} {mode}")
     amsgrad = variant == "amsgrad"
@@ -62,31 +51,30 @@ def test_bucket_2pow28_steady_state(variant, gdt, mode):
     g = synth.stored_grad(n, 1e-3, 1.0, gdt, key + ("g",), DEV)
     m, v, vmax = synth.steady_state(n, key, amsgrad, DEV, m_std=1e-4, v_root_std=1e-3)
     opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
-    idx = _sample_idx(n, 65536, (0, "bucket-sample"))
-    idx_dev = torch.from_numpy(idx).to(DEV)
-    before = [_gather(t, idx_dev) for t in (p, g, m, v, vmax)]
     if mode == "inplace":
+        pre = _clone((p, m, v, vmax))
         updated, step = ra.radamw_step_multi([ra.Segment(p, g, m, v, vmax)], 999, opts, ra.control(1.0))
         assert updated and step == 1000
         outs = (p, m, v, vmax)
     else:
+        pre = (p, m, v, vmax)
+        sums = [_bit_sum(t) for t in pre if t is not None]
         outs = (torch.empty_like(p), torch.empty_like(m), torch.empty_like(v),
                 torch.empty_like(vmax) if amsgrad else None)
         st_out = ra.AdamWState(0, outs[1], outs[2], outs[3])
         assert ra.radamw_step(p, g, ra.AdamWState(999, m, v, vmax), opts, ra.control(1.0), outs[0], st_out)
         assert st_out.step == 1000
-        # inputs untouched by an out-of-place step
-        assert bits_equal(_gather(p, idx_dev), before[0]) and bits_equal(_gather(m, idx_dev), before[2])
+        torch.cuda.synchronize()
+        assert [_bit_sum(t) for t in pre if t is not None] == sums  # inputs untouched
     torch.cuda.synchronize()
-    p_ref, st_ref = _oracle_on_sample(*before, 999, opts, 1.0, gdt)
-    after = [_gather(t, idx_dev) for t in outs]
-    contract_one_step(after[0].numpy(), p_ref, "p")
-    contract_one_step(after[1].numpy(), st_ref.exp_avg, "m")
-    contract_one_step(after[2].numpy(), st_ref.exp_avg_sq, "v")
+    stage = PinnedStage()
+    ref = oracle_one_step_pinned(stage, pre, g, gdt, oracle_opts(opts), 1.0, 999, amsgrad)
+    stats = {}
+    compare_one_step_full(f"bucket {variant} {gdt} {mode}", outs, ref, pre, g, 1.0, 0.9, 0.999,
+                          first=False, power_of_two=True, stats=stats)
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
     if amsgrad:
-        contract_one_step(after[3].numpy(), st_ref.max_exp_avg_sq, "vmax")
         assert bool(torch.all(outs[3] >= outs[2]))
-    assert bool(torch.isfinite(outs[0]).all()) and bool(torch.isfinite(outs[1]).all())
 
 
 def test_bucket_2pow28_fused_step_as_benched():
@@ -96,8 +84,8 @@ def test_bucket_2pow28_fused_step_as_benched():
     max_grad_norm = 1.0 (the norm is ~16.4, so the clip is active).  The
     report's count is the oracle's over all 2^28 gradients bit for bit and its
     sum lies within the oracle's sequential FP64 bound; the clip coefficient
-    is the oracle's rule applied to the report, bit for bit; sampled elements
-    (both ends and 64k random) match the oracle run at the clipped scale."""
+    is the oracle's rule applied to the report, bit for bit; every element
+    matches the oracle run at the clipped scale."""
     n = 1 << 28
     announce("bucket 2^28 fused step as benched")
     key = (0, "bucket", n)
@@ -107,8 +95,7 @@ def test_bucket_2pow28_fused_step_as_benched():
     opts = ra.options(lr=1e-3, weight_decay=1e-4)
     seglist = ra.SegmentList([ra.Segment(p, g, m, v, None)])
     ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=DEV)
-    idx_dev = torch.from_numpy(_sample_idx(n, 65536, (0, "bucket-fused-sample"))).to(DEV)
-    before = [_gather(t, idx_dev) for t in (p, g, m, v)]
+    pre = _clone((p, m, v, None))
     sumsq, count = oracle.grad_stats(grad_host(g), "f32")
     res, step = ra.radamw_fused_step_multi(seglist, 999, opts, 1.0, 1.0, True, ws)
     torch.cuda.synchronize()
@@ -119,16 +106,11 @@ def test_bucket_2pow28_fused_step_as_benched():
     assert res.clip_coef == clip and 0.0 < clip < 1.0
     skip, eff = oracle.decide(res.sumsq, res.nonfinite, 1.0, 1.0)
     assert not skip
-    p_ref, st_ref = _oracle_on_sample(*before, None, 999, opts, eff, "f32")
-    after = [_gather(t, idx_dev).numpy() for t in (p, m, v)]
-    contract_one_step(after[0], p_ref, "p")
-    contract_one_step(after[1], st_ref.exp_avg, "m")
-    contract_one_step(after[2], st_ref.exp_avg_sq, "v")
-    # the moments sit far below the absolute bar: bound them in ulps of the summed terms
-    g_unscaled = before[1].numpy().astype(np.float64) / eff
-    m_terms = np.abs(0.9 * before[2].numpy().astype(np.float64)) + np.abs(0.1 * g_unscaled)
-    ulps_of(after[1], st_ref.exp_avg, m_terms.astype(np.float32), 4, "m")
-    ulps_of(after[2], st_ref.exp_avg_sq, st_ref.exp_avg_sq, 8, "v")
+    ref = oracle_one_step_pinned(PinnedStage(), pre, g, "f32", oracle_opts(opts), eff, 999, False)
+    stats = {}
+    compare_one_step_full("fused bucket", (p, m, v, None), ref, pre, g, eff, 0.9, 0.999, first=False,
+                          power_of_two=False, stats=stats)
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
 
 
 def _decoder_segments(shapes, gdt, scale, amsgrad, step, key, std):
@@ -147,43 +129,92 @@ def _decoder_segments(shapes, gdt, scale, amsgrad, step, key, std):
     return segs
 
 
+def _seg_state(s):
+    return (s.param, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("odd", [False, True])
-def test_decoder_1b_list_one_launch_vs_per_tensor(odd):
+def test_decoder_1b_list_multi_call_vs_per_tensor(odd):
     """201 tensors shaped like a 1.1B decoder (odd variant: norms 2047/2049),
     FP16 grads N(0,1e-4)*1024 with scale 1024, AMSGrad, t = 50: one
-    radamw_step_multi launch == 201 radamw_step_inplace launches bit for bit,
-    and both match the oracle on sampled elements of every tensor."""
+    radamw_step_multi call (the 156 tensors of >= 2^22 elements launched
+    alone, the 45 norm vectors in one shared launch) equals 201
+    radamw_step_inplace launches bit for bit, and every element of every
+    tensor matches the oracle."""
     shapes = synth.decoder_1b_shapes(odd)
     announce(f"decoder 1.1B list odd={odd}")
     opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=True)
+    oo = oracle_opts(opts)
     scale = 1024.0
     segs = _decoder_segments(shapes, "f16", scale, True, 49, (0, "dec1b", odd), 1e-4)
     twins = [ra.Segment(s.param.clone(), s.grad, s.exp_avg.clone(), s.exp_avg_sq.clone(), s.max_exp_avg_sq.clone())
              for s in segs]
-    samples = []
-    for i, s in enumerate(segs):
-        n = s.param.numel()
-        idx = torch.from_numpy(_sample_idx(n, 2048, (0, "dec1b-sample", i))).to(DEV)
-        samples.append((idx, [_gather(t, idx) for t in (s.param, s.grad, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)]))
     launches = ra.radamw_launch_count()
     updated, step = ra.radamw_step_multi(segs, 49, opts, ra.control(scale))
-    # launch policy: tensors of >= 2^22 elements on their own, the rest share one launch
     solo = sum(1 for _, n in shapes if n >= 1 << 22)
     shared = sum(1 for _, n in shapes if n < 1 << 22)
     assert (solo, shared) == (156, 45)
     assert updated and step == 50 and ra.radamw_launch_count() == launches + solo + 1
-    for tw in twins:
-        assert ra.radamw_step_inplace(tw.param, tw.grad, ra.AdamWState(49, tw.exp_avg, tw.exp_avg_sq, tw.max_exp_avg_sq),
-                                      opts, ra.control(scale))
     torch.cuda.synchronize()
+    stage, stats = PinnedStage(), {}
     for i, (s, tw) in enumerate(zip(segs, twins)):
+        # the twin still holds the pre-step state: the oracle starts from it
+        ref = oracle_one_step_pinned(stage, _seg_state(tw), tw.grad, "f16", oo, scale, 49, True)
+        compare_one_step_full(shapes[i][0], _seg_state(s), ref, _seg_state(tw), s.grad, scale, 0.9, 0.999,
+                              first=False, power_of_two=True, stats=stats)
+        assert ra.radamw_step_inplace(tw.param, tw.grad, ra.AdamWState(49, tw.exp_avg, tw.exp_avg_sq,
+                                                                       tw.max_exp_avg_sq), opts, ra.control(scale))
+        torch.cuda.synchronize()
         assert bits_equal(s.param, tw.param) and bits_equal(s.exp_avg, tw.exp_avg), shapes[i][0]
         assert bits_equal(s.exp_avg_sq, tw.exp_avg_sq) and bits_equal(s.max_exp_avg_sq, tw.max_exp_avg_sq)
-        idx, before = samples[i]
-        p_ref, st_ref = _oracle_on_sample(*before, 49, opts, scale, "f16")
-        contract_one_step(_gather(s.param, idx).numpy(), p_ref, f"{shapes[i][0]} p")
-        contract_one_step(_gather(s.exp_avg, idx).numpy(), st_ref.exp_avg, f"{shapes[i][0]} m")
-        contract_one_step(_gather(s.max_exp_avg_sq, idx).numpy(), st_ref.max_exp_avg_sq, f"{shapes[i][0]} vmax")
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
+
+
+@pytest.mark.timeout(600)
+def test_decoder_1b_flattened_bucket():
+    """The 1.1B decoder's state as one flattened bucket (FA-ja
+    "サポートされている契約": a pre-flattened bucket, sharing options and the
+    step count): p, the FP16 gradient, m, v and v_max each one contiguous
+    allocation of 1,261,529,088 elements, updated by one radamw_step_multi
+    call over a single segment, i.e. one launch.  Every element matches the
+    oracle, and each tensor's slice equals a per-tensor launch over the same
+    slice of a twin arena bit for bit."""
+    shapes = synth.decoder_1b_shapes()
+    total = synth.total(shapes)
+    announce(f"decoder 1.1B flattened bucket ({total} params)")
+    opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=True)
+    oo = oracle_opts(opts)
+    scale = 1024.0
+    arena = [torch.empty(total, device=DEV), torch.empty(total, dtype=torch.float16, device=DEV)] + \
+        [torch.empty(total, device=DEV) for _ in range(3)]
+    spans, off = [], 0
+    for i, (_, n) in enumerate(shapes):
+        key = (0, "dec1b-flat", i)
+        arena[0][off:off + n] = synth.normal(n, 0.02, key + ("p",), DEV)
+        arena[1][off:off + n] = synth.stored_grad(n, 1e-4, scale, "f16", key + ("g",), DEV)
+        m, v, vmax = synth.steady_state(n, key, True, DEV, m_std=1e-5, v_root_std=1e-4)
+        arena[2][off:off + n], arena[3][off:off + n], arena[4][off:off + n] = m, v, vmax
+        spans.append((off, n))
+        off += n
+    twin = [t.clone() if k != 1 else t for k, t in enumerate(arena)]
+    launches = ra.radamw_launch_count()
+    updated, step = ra.radamw_step_multi([ra.Segment(*arena)], 49, opts, ra.control(scale))
+    assert updated and step == 50 and ra.radamw_launch_count() == launches + 1
+    torch.cuda.synchronize()
+    stage, stats = PinnedStage(), {}
+    for i, (o, n) in enumerate(spans):
+        a = [t[o:o + n] for t in arena]
+        b = [t[o:o + n] for t in twin]
+        pre = (b[0], b[2], b[3], b[4])
+        ref = oracle_one_step_pinned(stage, pre, b[1], "f16", oo, scale, 49, True)
+        compare_one_step_full(f"flat {shapes[i][0]}", (a[0], a[2], a[3], a[4]), ref, pre, a[1], scale, 0.9, 0.999,
+                              first=False, power_of_two=True, stats=stats)
+        assert ra.radamw_step_inplace(b[0], b[1], ra.AdamWState(49, b[2], b[3], b[4]), opts, ra.control(scale))
+    torch.cuda.synchronize()
+    for k in (0, 2, 3, 4):
+        assert bits_equal(arena[k], twin[k])
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
 
 
 def _oracle_stats(segs):
@@ -193,14 +224,15 @@ def _oracle_stats(segs):
     return acc.result
 
 
+@pytest.mark.timeout(900)
 def test_decoder_7b_list_stats_clip_skip_sequence():
     """291 tensors shaped like a 6.7B decoder, BF16 grads N(0,1e-4), scale 1,
     in-place AdamW from no state: fused step (stats -> hierarchical merge ->
     12-byte read-back -> clip at 1.0 -> update) at t = 1; then a step with
     round(1e-6 * N) = 6,738 injected +inf/NaN values, which must report
     exactly that count and skip; then a clean step at t = 2.  Statistics are
-    checked against the oracle over every element; the update on sampled
-    elements of every tensor."""
+    checked against the oracle over every element; each update over every
+    element, as one step from the state it started from."""
     shapes = synth.decoder_7b_shapes()
     total = synth.total(shapes)
     announce(f"decoder 6.7B list ({total} params)")
@@ -209,17 +241,13 @@ def test_decoder_7b_list_stats_clip_skip_sequence():
     segs = _decoder_segments(shapes, "bf16", 1.0, False, 0, (0, "dec7b"), 1e-4)
     ws = torch.empty(ra.radamw_fused_workspace_bytes(segs), dtype=torch.uint8, device=DEV)
     offsets = np.cumsum([0] + [n for _, n in shapes])
-    refs, idxs = [], []
-    for i, s in enumerate(segs):
-        idx = torch.from_numpy(_sample_idx(s.param.numel(), 512, (0, "dec7b-sample", i))).to(DEV)
-        idxs.append(idx)
-        refs.append((_gather(s.param, idx).numpy().copy(), oracle.State(idx.numel(), False)))
+    stage, stats = PinnedStage(), {}
 
     def fused(step, call):
         announce(f"decoder 6.7B fused call {call}")
         sumsq, count = _oracle_stats(segs)
         skip, eff = oracle.decide(sumsq, count, 1.0, 1.0)
-        grads = [_gather(s.grad, idx) for s, idx in zip(segs, idxs)]
+        pre = [_clone(_seg_state(s)) for s in segs] if not skip else None
         res, new_step = ra.radamw_fused_step_multi(segs, step, opts, 1.0, 1.0, True, ws)
         torch.cuda.synchronize()
         assert res.nonfinite == count and bool(res.found_inf) == skip
@@ -230,12 +258,14 @@ def test_decoder_7b_list_stats_clip_skip_sequence():
         # (pinned against fsum-exact sums in the statistics tests).
         assert abs(res.sumsq - sumsq) <= (total - 1) * 2.0**-53 * sumsq
         assert bool(res.updated) == (not skip) and new_step == step + (0 if skip else 1)
-        for (p_ref, st_ref), gr in zip(refs, grads):
-            oracle.adamw_step(p_ref, synth.grad_numpy(gr), "bf16", st_ref, oo, eff, skip)
-        for i, (s, idx) in enumerate(zip(segs, idxs)):
-            p_ref, st_ref = refs[i]
-            contract_one_step(_gather(s.param, idx).numpy(), p_ref, f"{shapes[i][0]} p call {call}")
-            contract_one_step(_gather(s.exp_avg_sq, idx).numpy(), st_ref.exp_avg_sq, f"{shapes[i][0]} v call {call}")
+        if not skip:
+            # the device decided with the report's own sum: the clip it applied
+            _, eff_dev = oracle.decide(res.sumsq, res.nonfinite, 1.0, 1.0)
+            for i, s in enumerate(segs):
+                ref = oracle_one_step_pinned(stage, pre[i], s.grad, "bf16", oo, eff_dev, step, False)
+                compare_one_step_full(f"{shapes[i][0]} call {call}", _seg_state(s), ref, pre[i], s.grad, eff_dev,
+                                      0.9, 0.999, first=step == 0, power_of_two=False, stats=stats)
+                pre[i] = None
         return res, new_step
 
     res, step = fused(0, 1)
@@ -251,31 +281,28 @@ def test_decoder_7b_list_stats_clip_skip_sequence():
             local = torch.from_numpy(pos[lo:hi] - offsets[i]).to(DEV)
             s.grad[local] = torch.tensor(vals[lo:hi], dtype=torch.bfloat16, device=DEV)
     launches = ra.radamw_launch_count()
-    snap = [s.param[:4096].clone() for s in segs]
-
-    def bit_sums():  # every word of p, m and v, summed as integers
-        return [tuple(int(t.view(torch.int32).sum(dtype=torch.int64)) for t in (s.param, s.exp_avg, s.exp_avg_sq))
-                for s in segs]
-
-    sums = bit_sums()
+    sums = [tuple(_bit_sum(t) for t in (s.param, s.exp_avg, s.exp_avg_sq)) for s in segs]
     res, step = fused(step, 2)
     assert res.found_inf and res.nonfinite == k == 6738 and step == 1 and not res.updated
-    assert all(bits_equal(a, s.param[:4096]) for a, s in zip(snap, segs))
     # statistics ran and the update kernels queued behind them read the skip and wrote nothing
     assert ra.radamw_launch_count() > launches
-    assert bit_sums() == sums
+    assert [tuple(_bit_sum(t) for t in (s.param, s.exp_avg, s.exp_avg_sq)) for s in segs] == sums
     # clean step at t = 2
     for i, s in enumerate(segs):
         s.grad.copy_(synth.stored_grad(s.grad.numel(), 1e-4, 1.0, "bf16", (0, "dec7b", i, "g3"), DEV))
     res, step = fused(step, 3)
     assert step == 2 and res.updated and not res.found_inf
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
 
 
+@pytest.mark.timeout(600)
 def test_single_tensor_beyond_32_bit_indexing():
     """One tensor of 2^32 + 1029 elements (64-bit indexing in every kernel):
-    in-place AdamW with BF16 grads at t = 3 and its statistics.  Oracle on
-    sampled elements around 2^31, 2^32 and the ragged end; statistics over
-    every element (count exact, sum within the sequential bound)."""
+    in-place AdamW with BF16 grads at t = 3 and its statistics, with one inf
+    past 2^32 and one NaN below 2^31.  Every element with a finite gradient
+    matches the oracle (a non-finite gradient is outside the formula's
+    contract); statistics over every element (count exact, sum within the
+    sequential bound)."""
     n = (1 << 32) + 1029
     announce(f"single tensor n={n}")
     p = synth.normal(n, 0.02, (0, "huge", "p"), DEV)
@@ -284,11 +311,6 @@ def test_single_tensor_beyond_32_bit_indexing():
     g[(1 << 32) + 17] = float("inf")
     g[(1 << 31) - 1] = float("nan")
     opts = ra.options(lr=1e-3, weight_decay=0.01)
-    rng = np.random.Generator(np.random.PCG64(11))
-    idx = np.unique(np.concatenate([np.arange(0, 512), np.arange((1 << 31) - 512, (1 << 31) + 512),
-                                    np.arange((1 << 32) - 512, n), rng.integers(0, n, 20000)]))
-    idx_dev = torch.from_numpy(idx).to(DEV)
-    before = [_gather(t, idx_dev) for t in (p, g, m, v, None)]
     # statistics over everything
     rows = ra.radamw_grad_stats_rows(n, torch.bfloat16)
     rows_buf = torch.zeros(3 * rows, dtype=torch.int32, device=DEV)
@@ -304,15 +326,16 @@ def test_single_tensor_beyond_32_bit_indexing():
     s_ref, c_ref = acc.result
     assert rep.nonfinite == c_ref == 2
     assert abs(rep.sumsq - s_ref) <= (n - 1) * 2.0**-53 * s_ref
-    # the update (non-finite elements are outside the formula's contract: masked below)
+    pre = _clone((p, m, v, None))
     updated, step = ra.radamw_step_multi([ra.Segment(p, g, m, v)], 2, opts, ra.control(1.0))
     assert updated and step == 3
     torch.cuda.synchronize()
-    p_ref, st_ref = _oracle_on_sample(*before, 2, opts, 1.0, "bf16")
-    x = torch.from_numpy(synth.grad_numpy(before[1]).view(np.int16)).view(torch.bfloat16).float().numpy()
-    ok = np.isfinite(x)
-    after_p = _gather(p, idx_dev).numpy()
-    after_v = _gather(v, idx_dev).numpy()
-    contract_one_step(after_p[ok], p_ref[ok], "p")
-    contract_one_step(after_v[ok], st_ref.exp_avg_sq[ok], "v")
-    assert ok.sum() == ok.size - 2
+    # the update is elementwise: the oracle takes the tensor in 2^28-element slices
+    stage = PinnedStage()
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        pre_c = tuple(None if t is None else t[lo:hi] for t in pre)
+        ref = oracle_one_step_pinned(stage, pre_c, g[lo:hi], "bf16", oracle_opts(opts), 1.0, 2, False)
+        compare_one_step_full(f"n = 2^32 + 1029, [{lo}, {hi})", (p[lo:hi], m[lo:hi], v[lo:hi], None), ref, pre_c,
+                              g[lo:hi], 1.0, 0.9, 0.999, first=False, power_of_two=True, finite_only=True)
+    assert int(torch.isfinite(g).logical_not().sum()) == 2

@@ -14,8 +14,8 @@ import oracle
 import synth
 import optimizer_step_dl_amd as ra
 from optimizer_step_dl_amd import _abi
-from gpu_helpers import (DEV, TORCH_GDT, announce, bits_equal, contract_one_step, grad_host, host,
-                         new_gpu_state, normwise, oracle_opts, snapshot, ulps_of, unchanged)
+from gpu_helpers import (DEV, TORCH_GDT, announce, bits_equal, check_step_from, clone_state, contract_one_step,
+                         grad_host, host, new_gpu_state, normwise, oracle_opts, snapshot, ulps_of, unchanged)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,10 @@ def test_fp32_adamw_ten_fresh_steps_65536():
     m_scale = np.zeros(n)
     for t, g in enumerate(grads, start=1):
         gd = g.to(DEV)
+        pre = clone_state(p_ip, st_ip)
         assert ra.radamw_step_inplace(p_ip, gd, st_ip, opts, ra.control(1.0))
+        torch.cuda.synchronize()
+        check_step_from(pre, clone_state(p_ip, st_ip), gd, "f32", opts, 1.0, t - 1, f"one step {t}")
         src_p, src_s = bufs[cur]
         dst_p, dst_s = bufs[1 - cur]
         assert ra.radamw_step(src_p, gd, src_s, opts, ra.control(1.0), dst_p, dst_s)
@@ -93,8 +96,13 @@ def test_bf16_amsgrad_hundred_calls_with_skips(n):
             torch.cuda.synchronize()
             before = snapshot(p, st.exp_avg, st.exp_avg_sq, st.max_exp_avg_sq)
             launches, step = ra.radamw_launch_count(), st.step
+        pre = clone_state(p, st) if call in (1, 50, 100) else None
+        step_before = st.step
         ran = ra.radamw_step_inplace(p, gd, st, opts, ra.control(128.0, skip))
         ran_ref = oracle.adamw_step(p_ref, grad_host(g), "bf16", st_ref, oo, 128.0, skip)
+        if pre is not None:
+            torch.cuda.synchronize()
+            check_step_from(pre, clone_state(p, st), gd, "bf16", opts, 128.0, step_before, f"one step, call {call}")
         assert ran == ran_ref == (not skip)
         if skip:
             torch.cuda.synchronize()
@@ -133,10 +141,13 @@ def test_matrix_five_steps_several_tiles(gdt, amsgrad, maximize):
     p_ref, st_ref = p0.numpy().copy(), oracle.State(n, amsgrad)
     for t in range(1, 6):
         g = synth.stored_grad(n, 1e-3 if t % 2 else 3e-2, scale, gdt, (0, "mx", gdt, "g", t))
-        assert ra.radamw_step_inplace(p, g.to(DEV), st, opts, ra.control(scale))
+        gd = g.to(DEV)
+        pre = clone_state(p, st)
+        assert ra.radamw_step_inplace(p, gd, st, opts, ra.control(scale))
         oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts), scale)
         torch.cuda.synchronize()
         _compare_state(p, st, p_ref, st_ref, amsgrad, f"t={t}", one_step=True)
+        check_step_from(pre, clone_state(p, st), gd, gdt, opts, scale, t - 1, f"one step t={t}")
 
 
 # ------------------------------------------------------------ tails --
@@ -155,9 +166,12 @@ def test_tail_lengths(gdt, amsgrad):
         p_ref, st_ref = p0.numpy().copy(), oracle.State(n, amsgrad)
         for t in (1, 2):
             g = synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "tail", n, "g", t))
-            ra.radamw_step_inplace(p, g.to(DEV), st, opts, ra.control())
+            gd = g.to(DEV)
+            pre = clone_state(p, st)
+            ra.radamw_step_inplace(p, gd, st, opts, ra.control())
             oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts))
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            check_step_from(pre, clone_state(p, st), gd, gdt, opts, 1.0, t - 1, f"n={n} one step t={t}")
         _compare_state(p, st, p_ref, st_ref, amsgrad, f"n={n}", one_step=True)
 
 
@@ -181,8 +195,11 @@ def test_views_at_offsets(phases):
     for t in (1, 2, 3):
         g = synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "off", "g", t))
         G[og:og + n].copy_(g.to(DEV))
+        pre = clone_state(p, st)
         ra.radamw_step_inplace(p, G[og:og + n], st, opts, ra.control())
         oracle.adamw_step(p_ref, grad_host(g), gdt, st_ref, oracle_opts(opts))
+        torch.cuda.synchronize()
+        check_step_from(pre, clone_state(p, st), G[og:og + n], gdt, opts, 1.0, t - 1, f"phases {phases} t={t}")
     torch.cuda.synchronize()
     _compare_state(p, st, p_ref, st_ref, True, f"phases {phases}", one_step=True)
     # nothing outside the views was written
@@ -220,10 +237,16 @@ def test_multi_tensor_one_launch_matches_oracle_and_per_tensor(gdt, amsgrad):
             s.grad.copy_(g.to(DEV))
             tw.grad.copy_(s.grad)
             oracle.adamw_step(refs[i][0], grad_host(g), gdt, refs[i][1], oracle_opts(opts), scale)
+        pres = [clone_state(s.param, ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)) for s in segs]
         before = ra.radamw_launch_count()
         updated, step = ra.radamw_step_multi(segs, step, opts, ra.control(scale))
         assert updated and step == t
         assert ra.radamw_launch_count() == before + 1
+        torch.cuda.synchronize()
+        for i, (s, pre) in enumerate(zip(segs, pres)):
+            if sizes[i]:
+                after = (s.param, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)
+                check_step_from(pre, after, s.grad, gdt, opts, scale, t - 1, f"segment {i} one step t={t}")
         for tw, ts in zip(twins, twin_states):
             ra.radamw_step_inplace(tw.param, tw.grad, ts, opts, ra.control(scale))
     torch.cuda.synchronize()
@@ -326,8 +349,15 @@ def test_random_lists_match_per_tensor_launches(seed, gdt, amsgrad):
             tw.grad.copy_(s.grad)
             if refs[i] is not None and sizes[i]:
                 oracle.adamw_step(refs[i][0], grad_host(g), gdt, refs[i][1], oracle_opts(opts), scale)
+        pres = [clone_state(s.param, ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)) for s in segs]
+        step_before = step
         updated, step = ra.radamw_step_multi(segs, step, opts, ra.control(scale))
         assert updated == any(sizes) and step == (t if any(sizes) else 0)
+        torch.cuda.synchronize()
+        for i, (s, pre) in enumerate(zip(segs, pres)):
+            if sizes[i]:
+                after = (s.param, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)
+                check_step_from(pre, after, s.grad, gdt, opts, scale, step_before, f"tensor {i} one step t={t}")
         for tw, ts in zip(twins, twin_states):
             ra.radamw_step_inplace(tw.param, tw.grad, ts, opts, ra.control(scale))
     torch.cuda.synchronize()

@@ -15,12 +15,17 @@ events (radamw_time_next_update: hipExtLaunchKernelGGL on the launch stream)
 give the kernel duration the roofline object uses.
 
 Prints ONE JSON line (rank 0).  Extra keys beside the contract's:
-"roofline", "cpu_baseline", "cpu_baseline_all_cores", "kernels" (update
-kernel timing, rest of the step), "device" (GPU, versions, clocks), "variants" (update-only timings of the bucket's other
-configurations), "staged_vs_fused" (the pages' staged baseline A/B),
-"decoder_1b_list" (per-tensor vs radamw_step_multi launches),
-"decoder_7b_fused_step" (the whole step over a 6.7B-parameter list),
-"copy_ceiling" (torch elementwise copy bandwidth, context only).
+"roofline" (with the update's fraction of the measured streaming ceiling),
+"cpu_baseline", "cpu_baseline_threads", "kernels" (update kernel timing, rest
+of the step), "stream_ceiling" (radamw_stream_probe: the update's access
+pattern with trivial arithmetic), "device" (GPU, versions, clocks from
+sysfs), "provenance" (command line, commit, source and library hashes),
+"variants" (update-only timings of the bucket's other configurations),
+"staged_vs_fused" (the pages' staged baseline A/B), "decoder_1b_list"
+(per-tensor launches, the multi-tensor call over the list, and one
+flattened bucket), "decoder_7b_fused_step" (the whole step over a
+6.7B-parameter list), "fusedadamw_1b" (the torch optimizer),
+"copy_calibration" (torch's copy kernel used to scale the HBM counters).
 """
 from __future__ import annotations
 
@@ -127,7 +132,7 @@ def main(argv=None):
     n = args.n
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs, n={n}")
-    smi_before = smi_snapshot()
+    smi_before = clock_snapshot(props)
 
     # ---------------------------------------------------- headline step --
     p, g, m, v, _ = build_inputs(torch, synth, n, "adamw", "f32", dev)
@@ -188,6 +193,11 @@ def main(argv=None):
     del p, g, m, v, ws, seglist
     torch.cuda.empty_cache()
 
+    # ------------------------------------- streaming ceiling of the pattern --
+    ceiling = bench_stream_ceiling(torch, ra, dev, stream, n)
+    ceil_gbs = ceiling["adamw_4r3w"]["gbs"]
+    log(f"update / 4-read 3-write ceiling: {achieved / ceil_gbs:.4f}")
+
     # ------------------------------------------------ update-only variants --
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
@@ -247,7 +257,6 @@ def main(argv=None):
             del outs, sets
         torch.cuda.empty_cache()
 
-    # --------------------------------------------------- copy ceiling --
     # ------------------------------- staged baseline A/B (the pages' bench) --
     staged = None
     if args.variants == "all" or "staged" in args.variants.split(","):
@@ -269,8 +278,8 @@ def main(argv=None):
         optim_1b = bench_optimizer_1b(torch, synth, ra, dev, stream)
 
     # A plain elementwise copy of known size (1 GiB read, 1 GiB written):
-    # torch's unary negation kernel.  It is the calibration kernel for the
-    # rocprofv3 HBM counters and, timed, a context ceiling for streaming.
+    # torch's unary negation kernel, the calibration kernel for the rocprofv3
+    # HBM counters (timed too, for context: torch's own launch geometry).
     copy_ceiling = None
     if args.copy_calibration or wanted:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -285,9 +294,9 @@ def main(argv=None):
         e1.record(stream)
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / 10
-        copy_ceiling = {"kernel": "torch.neg (elementwise copy)", "bytes": 2 * a.numel() * 4, "avg_ms": cms,
+        copy_ceiling = {"kernel": "torch.neg (elementwise copy, counter calibration)", "bytes": 2 * a.numel() * 4, "avg_ms": cms,
                         "gbs": 2 * a.numel() * 4 / (cms * 1e-3) / 1e9}
-        log(f"copy ceiling: {copy_ceiling['gbs']:.0f} GB/s")
+        log(f"copy calibration kernel: {copy_ceiling['gbs']:.0f} GB/s")
         del a, b
 
     # --------------------------------------------------- CPU oracle --
@@ -319,23 +328,66 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "adamw_update_single<f32, adamw, steady>",
-                     "algorithmic_bytes_per_launch": bpp * n},
+                     "algorithmic_bytes_per_launch": bpp * n,
+                     "stream_ceiling_gbs": ceil_gbs, "frac_of_stream_ceiling": achieved / ceil_gbs,
+                     "stream_ceiling_kernel": "stream_probe<4, 3> (4-read / 3-write, the update's geometry)"},
         "cpu_baseline": cpu,
-        "cpu_baseline_all_cores": cpu_all,
+        "cpu_baseline_threads": cpu_all,
         "kernels": kernels,
         "variants": variants,
-        "copy_ceiling": copy_ceiling,
+        "stream_ceiling": ceiling,
+        "copy_calibration": copy_ceiling,
         "decoder_1b_list": decoder,
         "staged_vs_fused": staged,
         "decoder_7b_fused_step": decoder7,
         "fusedadamw_1b": optim_1b,
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": torch.version.hip,
-                   "memory_bytes": props.total_memory, "rocm_smi_before": smi_before,
-                   "rocm_smi_after": smi_snapshot()},
+                   "memory_bytes": props.total_memory, "clocks_before": smi_before,
+                   "clocks_after": clock_snapshot(props)},
+        "provenance": provenance(sys.argv if argv is None else ["bench.py", *argv]),
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+STREAM_PATTERNS = (("read_only_1r", 1, 0), ("write_only_1w", 0, 1), ("copy_1r1w", 1, 1),
+                   ("first_step_2r3w", 2, 3), ("adamw_4r3w", 4, 3), ("amsgrad_5r4w", 5, 4))
+
+
+def bench_stream_ceiling(torch, ra, dev, stream, n, reps=20):
+    """radamw_stream_probe over n-element FP32 streams, each a separate
+    allocation like the bucket's: the update kernel's geometry, cache hints
+    and occupancy rule with one add per stream instead of the optimizer's
+    arithmetic.  The 4-read / 3-write pattern is the AdamW update's, 5 / 4
+    AMSGrad's, 2 / 3 a first step's.  Kernel start / end events per launch,
+    averaged over `reps` launches."""
+    ins = [torch.full((n,), 1.0 + k, dtype=torch.float32, device=dev) for k in range(5)]
+    outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(4)]
+    out = {}
+    for name, nr, nw in STREAM_PATTERNS:
+        args = (ins[:nr], outs[:nw], 0, outs[0] if nw == 0 else None)
+        for _ in range(3):
+            ra.radamw_stream_probe(*args)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for a, b in ev:
+            ra.radamw_time_next_update(a, b)
+            ra.radamw_stream_probe(*args)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)
+        avg = sum(ms) / len(ms)
+        nbytes = 4 * (nr + nw) * n
+        out[name] = {"reads": nr, "writes": nw, "bytes_per_element": 4 * (nr + nw), "avg_ms": avg,
+                     "min_ms": ms[0], "gbs": nbytes / (avg * 1e-3) / 1e9}
+        log(f"stream ceiling {name}: {avg:.4f} ms, {out[name]['gbs']:.0f} GB/s")
+    del ins, outs
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_staged(torch, synth, ra, dev, stream, n):
@@ -553,11 +605,42 @@ def bench_optimizer_1b(torch, synth, ra, dev, stream):
     return out
 
 
+def decoder_1b_flat(torch, synth, ra, dev, shapes, key0):
+    """The 1.1B decoder's state as one flattened bucket: p, the FP16
+    gradient, m, v and v_max are each one contiguous allocation of all
+    1,261,529,088 elements, filled tensor by tensor with the list's own draws
+    (FP32 masters N(0, 0.02), FP16 gradients N(0, 1e-4) x 1024, m ~ N(0,
+    1e-5), v = N(0, 1e-4)^2, v_max = v U(1, 1.5)).  Returns the five arenas
+    and each tensor's (offset, size)."""
+    total = synth.total(shapes)
+    arena = [torch.empty(total, dtype=torch.float32, device=dev),
+             torch.empty(total, dtype=torch.float16, device=dev)] + \
+            [torch.empty(total, dtype=torch.float32, device=dev) for _ in range(3)]
+    spans, off = [], 0
+    for i, (_, n) in enumerate(shapes):
+        key = key0 + (i,)
+        arena[0][off:off + n] = synth.normal(n, 0.02, key + ("p",), dev)
+        arena[1][off:off + n] = synth.stored_grad(n, 1e-4, 1024.0, "f16", key + ("g",), dev)
+        m, v, vmax = synth.steady_state(n, key, True, dev, m_std=1e-5, v_root_std=1e-4)
+        arena[2][off:off + n], arena[3][off:off + n], arena[4][off:off + n] = m, v, vmax
+        spans.append((off, n))
+        off += n
+    return arena, spans
+
+
 def bench_decoder_list(torch, synth, ra, dev, stream):
     """201 tensors shaped like a 1.1B decoder, FP16 grads (N(0,1e-4) x 1024,
-    scale 1024), AMSGrad at t = 50: 201 per-tensor launches (the pages'
-    torch front-end launches one update kernel per parameter) against one
-    radamw_step_multi launch over the same list."""
+    scale 1024), AMSGrad at t = 50 (34 B/param), four ways:
+      per_tensor   201 radamw_step_inplace calls (the pages' torch front-end
+                   launches one update kernel per parameter);
+      multi_list   one radamw_step_multi call over the 201 separately
+                   allocated tensors: 156 large tensors launched alone, the
+                   45 norm vectors in one shared launch, over two streams;
+      multi_views  the same call over 201 views of one contiguous arena per
+                   stream (the same launch split);
+      flat_bucket  one radamw_step_multi call over the arena as a single
+                   segment: one launch of 1,261,529,088 elements (the pages'
+                   pre-flattened bucket, which shares options and step)."""
     shapes = synth.decoder_1b_shapes()
     n_total = synth.total(shapes)
     segs = []
@@ -567,23 +650,31 @@ def bench_decoder_list(torch, synth, ra, dev, stream):
         g = synth.stored_grad(n, 1e-4, 1024.0, "f16", key + ("g",), dev)
         m, v, vmax = synth.steady_state(n, key, True, dev, m_std=1e-5, v_root_std=1e-4)
         segs.append(ra.Segment(p, g, m, v, vmax))
+    arena, spans = decoder_1b_flat(torch, synth, ra, dev, shapes, (0, "dec1b-bench"))
+    views = [ra.Segment(*[a[o:o + n] for a in arena]) for o, n in spans]
+    flat = [ra.Segment(*arena)]
     opts = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=True)
     ctrl = ra.control(1024.0)
     states = [ra.AdamWState(49, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq) for s in segs]
+    lists = {"multi_list": ra.SegmentList(segs), "multi_views": ra.SegmentList(views),
+             "flat_bucket": ra.SegmentList(flat)}
 
     def per_tensor():
         for s, st in zip(segs, states):
             st.step = 49
             ra.radamw_step_inplace(s.param, s.grad, st, opts, ctrl)
 
-    def one_launch():
-        ra.radamw_step_multi(segs, 49, opts, ctrl)
-
+    arms = [("per_tensor", per_tensor)] + [(k, (lambda sl: lambda: ra.radamw_step_multi(sl, 49, opts, ctrl))(sl))
+                                           for k, sl in lists.items()]
     out = {"tensors": len(shapes), "n_params": n_total, "bytes_per_param": 34}
-    for name, fn in (("per_tensor", per_tensor), ("one_launch", one_launch)):
+    for name, fn in arms:
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
+        launches = ra.radamw_launch_count()
+        fn()
+        torch.cuda.synchronize()
+        launches = ra.radamw_launch_count() - launches
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
@@ -593,10 +684,12 @@ def bench_decoder_list(torch, synth, ra, dev, stream):
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / 10
         ms = e0.elapsed_time(e1) / 10
-        out[name] = {"device_ms": ms, "wall_ms": wall * 1e3, "params_per_s": n_total / (ms * 1e-3),
-                     "gbs": 34 * n_total / (ms * 1e-3) / 1e9}
-        log(f"decoder 1.1B list {name}: {ms:.3f} ms device, {wall * 1e3:.3f} ms wall, {out[name]['gbs']:.0f} GB/s")
-    del segs, states
+        gbs = 34 * n_total / (ms * 1e-3) / 1e9
+        out[name] = {"device_ms": ms, "wall_ms": wall * 1e3, "launches_per_step": launches,
+                     "params_per_s": n_total / (ms * 1e-3), "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+        log(f"decoder 1.1B list {name}: {launches} launches, {ms:.3f} ms device, {wall * 1e3:.3f} ms wall, "
+            f"{gbs:.0f} GB/s")
+    del segs, states, lists, views, flat, arena
     torch.cuda.empty_cache()
     return out
 
@@ -637,16 +730,21 @@ def cpu_baseline(torch, synth, seconds):
             "bytes_per_param_model": 28}
 
 
+CPU_SHARE = 16  # host threads one GPU's job is given on the measurement boxes
+
+
 def cpu_baseline_threads(torch, synth, seconds):
-    """The same oracle step on all host cores this process may use (at most
-    16): the element range is split into one contiguous slice per thread and
+    """The same oracle step on as many threads as the process may use, at
+    most CPU_SHARE (the CPU share of one GPU's job; the record also states
+    the affinity mask and the machine's CPU count): the element range is split into one contiguous slice per thread and
     every thread runs the oracle's own scalar loops on its slice (ctypes
     releases the GIL).  The update is elementwise, so the slices compute
     exactly what one call would; the per-slice sums of squares are added
     afterwards, which changes only their FP64 rounding order."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(CPU_SHARE, affinity))
     n = 1 << 24
     p, g, st = _cpu_sample(synth, n)
     opts = oracle.Options(lr=1e-3, weight_decay=1e-4)
@@ -670,28 +768,108 @@ def cpu_baseline_threads(torch, synth, seconds):
                 break
     log(f"cpu oracle on {cores} threads: {steps} steps of {n} elements in {el:.1f} s")
     return {"value": n * steps / el, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "cpu_share_cap": CPU_SHARE, "affinity_cpus": affinity, "os_cpu_count": os.cpu_count(),
             "sample": f"first 2^24 = {n:,} elements of the same bucket recipe, full step, element range split "
                       f"into {cores} contiguous slices (one thread each), {steps} steps in {el:.1f} s"}
 
 
-def smi_snapshot():
-    """Clocks, power, DPM performance level, temperature, GPU and memory use
-    and driver version as rocm-smi reports them (best effort; None if the
-    tool is missing or says nothing).  Taken before and after the timed work,
-    so that the record shows the settings and any other load on the GPU."""
-    import subprocess
+def _read(path):
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showperflevel", "--showtemp",
-                              "--showuse", "--showmemuse", "--showdriverversion", "--json"],
-                             capture_output=True, text=True, timeout=30)
-        data = json.loads(out.stdout)
-        snap = {}
-        for name, fields in data.items():
-            if isinstance(fields, dict):
-                snap.update({k.strip(): v for k, v in fields.items()})
-        return snap or None
-    except Exception:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
         return None
+
+
+def _gpu_sysfs_dir(props):
+    """sysfs directory of the device torch calls cuda:0, found by its PCI
+    address; None when the box exposes no amdgpu sysfs for it."""
+    addr = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    d = os.path.join("/sys/bus/pci/devices", addr)
+    return d if os.path.exists(os.path.join(d, "pp_dpm_sclk")) else None
+
+
+def clock_snapshot(props):
+    """Clocks, DPM performance level, temperatures, power, GPU / memory
+    activity and the driver version, read in-process from the amdgpu sysfs
+    files of the benchmarked device (no child process: under a profiler's
+    preload a spawned tool would initialise the GPU itself).  Taken before
+    and after the timed work.  None when sysfs does not expose the device."""
+    d = _gpu_sysfs_dir(props)
+    if d is None:
+        return None
+
+    def current(level_file):
+        text = _read(os.path.join(d, level_file))
+        if not text:
+            return None
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                return line.split(":", 1)[-1].replace("*", "").strip()
+        return None
+
+    snap = {"sysfs": d, "sclk": current("pp_dpm_sclk"), "mclk": current("pp_dpm_mclk"),
+            "fclk": current("pp_dpm_fclk"), "socclk": current("pp_dpm_socclk"),
+            "perf_level": _read(os.path.join(d, "power_dpm_force_performance_level")),
+            "gpu_busy_percent": _read(os.path.join(d, "gpu_busy_percent")),
+            "mem_busy_percent": _read(os.path.join(d, "mem_busy_percent")),
+            "driver": _read("/sys/module/amdgpu/version")}
+    hw = os.path.join(d, "hwmon")
+    try:
+        for h in sorted(os.listdir(hw)):
+            base = os.path.join(hw, h)
+            for f in sorted(os.listdir(base)):
+                if f.startswith("temp") and f.endswith("_input"):
+                    label = _read(os.path.join(base, f.replace("_input", "_label"))) or f
+                    val = _read(os.path.join(base, f))
+                    if val is not None:
+                        snap[f"temp_{label}_C"] = int(val) / 1000.0
+                elif f in ("power1_average", "power1_input"):
+                    val = _read(os.path.join(base, f))
+                    if val is not None:
+                        snap[f"{f}_W"] = int(val) / 1e6
+    except OSError:
+        pass
+    return snap
+
+
+def provenance(argv):
+    """What produced this record: the command line, the commit (when the
+    tree carries its .git directory), hashes of the update kernel's code and
+    of every product source file, and of the library that was loaded."""
+    def git_head():
+        head = _read(os.path.join(HERE, ".git", "HEAD"))
+        if not head:
+            return None
+        if not head.startswith("ref:"):
+            return head
+        ref = head.split(None, 1)[1]
+        val = _read(os.path.join(HERE, ".git", ref))
+        if val:
+            return val
+        packed = _read(os.path.join(HERE, ".git", "packed-refs")) or ""
+        for line in packed.splitlines():
+            if line.endswith(" " + ref):
+                return line.split()[0]
+        return None
+
+    h = hashlib.sha256()
+    files = []
+    for sub in ("include", os.path.join("optimizer_step_dl_amd", "csrc"), "optimizer_step_dl_amd", "synth"):
+        base = os.path.join(HERE, sub)
+        for f in sorted(os.listdir(base)):
+            if f.endswith((".h", ".hip", ".cpp", ".py")):
+                files.append(os.path.join(sub, f))
+    files.append("bench.py")
+    for rel in files:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    lib = os.path.join(HERE, "optimizer_step_dl_amd", "libradamw.so")
+    with open(lib, "rb") as f:
+        lib_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {"argv": list(argv), "git_commit": git_head(), "kernel_source_sha256_16": kernel_source_hash(),
+            "source_tree_sha256_16": h.hexdigest()[:16], "source_files": len(files),
+            "library_sha256_16": lib_hash}
 
 
 if __name__ == "__main__":

@@ -19,9 +19,9 @@
  *     the work was SUBMITTED, not that it completed (FA-ja "低レベルの使用").
  *     The caller keeps every buffer alive until the stream has passed the
  *     work, and synchronises before reading results or saving a checkpoint.
- *   - Any non-zero return other than RADAMW_ERR_HIP means nothing was
- *     launched and nothing (device memory, state structs, step counts,
- *     output flags) was modified (FA-ja "低レベルの使用": validation leaves
+ *   - Any non-zero return other than RADAMW_ERR_HIP and RADAMW_ERR_DECISION
+ *     means nothing was launched and nothing (device memory, state structs,
+ *     step counts, output flags) was modified (FA-ja "低レベルの使用": validation leaves
  *     every input unchanged).  RADAMW_ERR_HIP reports a failing HIP runtime
  *     call; a multi-kernel entry point may have submitted earlier kernels,
  *     and the caller should treat the device state as unconfirmed (FA-ja
@@ -68,8 +68,15 @@ enum {
     RADAMW_ERR_RANGE = -5,   /* row count / capacity / scratch size out of
                                 range; an element count above 2^48 (any
                                 entry point taking n)                         */
-    RADAMW_ERR_HIP = -6      /* a HIP runtime call failed (see
+    RADAMW_ERR_HIP = -6,     /* a HIP runtime call failed (see
                                 radamw_last_hip_error)                         */
+    RADAMW_ERR_DECISION = -7 /* fused steps only: the host's skip / clip
+                                decision from the read-back report differs
+                                from the one the device took and applied (a
+                                library fault; never expected).  Unlike the
+                                other errors the step DID run as the device
+                                decided: the result struct and the step count
+                                follow the device's decision.                 */
 };
 
 /* Gradient storage type (FA-zh "增加的实际能力"). */
@@ -205,6 +212,33 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
  * radamw_step_inplace.  Every array must be 16-byte aligned (RADAMW_ERR_ALIGN),
  * gradients of 16-bit types 8-byte aligned.
  */
+/*
+ * Streaming ceiling, for measurement only.  FA-ja "残りゲート" asks that
+ * performance work follow measured profiles rather than the traffic model;
+ * this call measures what the memory system gives the update's access
+ * pattern.  It moves nreads FP32 read streams and nwrites FP32 write streams
+ * of n elements with the update kernel's geometry, cache hints and
+ * occupancy rule, and one add per stream instead of the optimizer's
+ * arithmetic: out[w][i] = ((in[0][i] + in[1][i]) + ...) + w (the empty sum
+ * is 0).  AdamW with an FP32 gradient is the 4-read / 3-write pattern,
+ * AMSGrad 5 / 4, a first step 2 / 3.
+ *   in        : host array of nreads device pointers (0 <= nreads <= 5).
+ *   out       : host array of max(nwrites, 1) device pointers
+ *               (0 <= nwrites <= 4).  With nwrites == 0, out[0] is a sink of
+ *               n floats that is never written in practice (a store guarded
+ *               by a comparison with NaN keeps the loads live).
+ *   n         : elements per stream, a multiple of 4; every array 16-byte
+ *               aligned (RADAMW_ERR_ALIGN).
+ *   cap_per_cu: resident workgroups per compute unit, 1..32, or 0 for the
+ *               update kernels' own rule applied to 4 * (nreads + nwrites)
+ *               bytes per element.
+ * nreads + nwrites >= 1.  Written arrays may overlap nothing
+ * (RADAMW_ERR_ALIAS); read arrays may overlap each other.  n == 0 launches
+ * nothing.  radamw_time_next_update applies to this launch.
+ */
+int radamw_stream_probe(const float *const *in, int32_t nreads, float *const *out, int32_t nwrites,
+                        int64_t n, int32_t cap_per_cu, radamw_stream_t stream);
+
 int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
                                radamw_state *st, float *delta, const radamw_options *opts,
                                const radamw_control *ctrl, radamw_stream_t stream,
@@ -325,6 +359,22 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale,
                   radamw_fused_result *result);
 
 /*
+ * The check every fused step makes after its read-back (TR-zh "在 ruda:0 上
+ * 进行原生 PyTorch 训练": the report read back decides whether and how the
+ * step updates): the host's decision from host_report (radamw_decide) must
+ * equal the device's, device_decision = {skip, bits of the FP32 unscale
+ * factor 1 / (gradient_scale / clip)} as the final merge wrote it.  result
+ * (host, required) is filled from the report as by radamw_decide, with
+ * result->updated taken from the DEVICE's decision, which is the one the
+ * queued update kernels applied.  Returns RADAMW_OK when the two agree
+ * (same skip; for an update, the same FP32 factor bit for bit) and
+ * RADAMW_ERR_DECISION otherwise.  Host only.
+ */
+int radamw_check_decision(const radamw_stats *host_report, const uint32_t *device_decision,
+                          double gradient_scale, double max_grad_norm,
+                          radamw_fused_result *result);
+
+/*
  * The whole fused step over a tensor list, the ruda_torch.AdamW
  * fused_step path of TR-zh: statistics of every active gradient ->
  * (hierarchical) merge -> 12-byte report read back -> skip or clip decision
@@ -344,9 +394,11 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale,
  * the decision itself and advances *step when the update ran.  When the
  * report counts a non-finite value the queued update kernels write nothing
  * (they have already issued their reads, so a skipped step costs one read
- * pass; skips are rare).  The two decisions always agree; if they did not,
- * the call would return RADAMW_ERR_HIP.  The workspace stays in use until
- * the stream has passed the update kernels.
+ * pass of the update's inputs; skips are rare).  The two decisions always
+ * agree (radamw_check_decision); if they did not, the call returns
+ * RADAMW_ERR_DECISION with *step and *result following the decision the
+ * device applied.  The workspace stays in use until the stream has passed
+ * the update kernels.
  */
 int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg,
                                      radamw_dtype gdt);

@@ -39,6 +39,20 @@ class RadamwError(RuntimeError):
         super().__init__(f"{where}: {msg} [{status}]{extra}")
 
 
+RADAMW_ERR_DECISION = -7
+
+
+class DecisionMismatch(RadamwError):
+    """RADAMW_ERR_DECISION from a fused step: the host's decision differed
+    from the device's, and the step ran as the device decided.  ``result``
+    and ``step`` (or ``steps``) are what the call reported, so the caller's
+    step counts can follow the state that was written."""
+
+    def __init__(self, where: str, result, step=None, steps=None):
+        super().__init__(RADAMW_ERR_DECISION, where)
+        self.result, self.step, self.steps = result, step, steps
+
+
 # ----------------------------------------------------------------- structs --
 
 class Options(ctypes.Structure):
@@ -137,6 +151,7 @@ def load(path: str = LIB_PATH):
         "radamw_step_multi": ([P(_Segment), i32, i32, P(u64), P(Options), P(Control), vp, P(i32)], ctypes.c_int),
         "radamw_step_staged_inplace": ([vp, vp, i32, i64, P(_State), vp, P(Options), P(Control), vp, P(i32)],
                                        ctypes.c_int),
+        "radamw_stream_probe": ([P(vp), i32, P(vp), i32, i64, i32, vp], ctypes.c_int),
         "radamw_step_multi_writeback": ([P(_Segment), P(vp), i32, i32, i32, P(u64), P(Options), P(Control), vp,
                                          P(i32)], ctypes.c_int),
         "radamw_stats_plan": ([i64, P(i64), P(i32)], ctypes.c_int),
@@ -145,6 +160,7 @@ def load(path: str = LIB_PATH):
         "radamw_merge_stats": ([vp, i64, vp, i64, vp, i32, vp], ctypes.c_int),
         "radamw_read_report": ([vp, P(Stats), vp], ctypes.c_int),
         "radamw_decide": ([P(Stats), dbl, dbl, P(Control), P(FusedResult)], ctypes.c_int),
+        "radamw_check_decision": ([P(Stats), P(ctypes.c_uint32), dbl, dbl, P(FusedResult)], ctypes.c_int),
         "radamw_fused_workspace_bytes": ([P(_Segment), i32, i32], i64),
         "radamw_fused_step_multi": ([P(_Segment), i32, i32, P(u64), P(Options), dbl, dbl, i32, vp, i64, vp,
                                      P(FusedResult)], ctypes.c_int),
@@ -169,9 +185,9 @@ def load(path: str = LIB_PATH):
 
 
 EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "radamw_step_multi",
-           "radamw_step_staged_inplace", "radamw_step_multi_writeback",
+           "radamw_step_staged_inplace", "radamw_stream_probe", "radamw_step_multi_writeback",
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
-           "radamw_read_report", "radamw_decide", "radamw_fused_workspace_bytes",
+           "radamw_read_report", "radamw_decide", "radamw_check_decision", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
            "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update",
            "radamw_list_create", "radamw_list_step", "radamw_list_fused_step", "radamw_list_destroy",
@@ -361,6 +377,30 @@ def radamw_step_staged_inplace(param: torch.Tensor, grad: torch.Tensor, state: A
     return bool(updated.value)
 
 
+def radamw_stream_probe(ins: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], cap_per_cu: int = 0,
+                        sink: Optional[torch.Tensor] = None) -> None:
+    """Streaming ceiling (measurement only): len(ins) FP32 read streams and
+    len(outs) write streams with the update kernel's geometry;
+    outs[w] = sum(ins) + w.  With no output, ``sink`` (an FP32 tensor of the
+    streams' size) is the never-written sink."""
+    lib = load()
+    tensors = list(ins) + list(outs) + ([] if sink is None else [sink])
+    if not tensors:
+        raise ValueError("at least one stream")
+    dev = tensors[0].device
+    n = tensors[0].numel()
+    for i, t in enumerate(tensors):
+        _dense(t, f"stream {i}", torch.float32, n, dev)
+    if not outs and sink is None:
+        raise ValueError("a read-only probe needs a sink tensor")
+    pin = (ctypes.c_void_p * max(1, len(ins)))(*[t.data_ptr() for t in ins])
+    wr = list(outs) if outs else [sink]
+    pout = (ctypes.c_void_p * len(wr))(*[t.data_ptr() for t in wr])
+    with torch.cuda.device(dev):
+        rc = lib.radamw_stream_probe(pin, len(ins), pout, len(outs), n, int(cap_per_cu), _stream(dev))
+    _check(rc, "radamw_stream_probe")
+
+
 def radamw_step_multi(segments, step: int, opts: Options, ctrl: Control):
     """In-place update of a tensor list (a sequence of Segment or a
     SegmentList) sharing options and step count.  Returns (updated, new_step)."""
@@ -478,6 +518,20 @@ def radamw_decide(host_report: Stats, gradient_scale: float, max_grad_norm: Opti
     return ctrl, res
 
 
+def radamw_check_decision(host_report: Stats, device_skip: int, device_inv_scale_bits: int,
+                          gradient_scale: float, max_grad_norm: Optional[float]):
+    """(agree, FusedResult): the host's decision from ``host_report`` against
+    a device decision {skip, bits of the FP32 unscale factor}; the result's
+    ``updated`` follows the device's."""
+    dec = (ctypes.c_uint32 * 2)(int(device_skip) & 0xffffffff, int(device_inv_scale_bits) & 0xffffffff)
+    res = FusedResult()
+    rc = load().radamw_check_decision(ctypes.byref(host_report), dec, float(gradient_scale),
+                                      0.0 if max_grad_norm is None else float(max_grad_norm), ctypes.byref(res))
+    if rc not in (RADAMW_OK, RADAMW_ERR_DECISION):
+        _check(rc, "radamw_check_decision")
+    return rc == RADAMW_OK, res
+
+
 def radamw_fused_workspace_bytes(segments) -> int:
     arr, code, _, count = _marshal(segments)
     r = load().radamw_fused_workspace_bytes(arr, count, code)
@@ -503,6 +557,8 @@ def radamw_fused_step_multi(segments, step: int, opts: Options,
             0.0 if max_grad_norm is None else float(max_grad_norm), int(bool(hierarchical)),
             _ptr_or_none(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
             _stream(dev), ctypes.byref(res))
+    if rc == RADAMW_ERR_DECISION:
+        raise DecisionMismatch("radamw_fused_step_multi", res, step=int(st.value))
     _check(rc, "radamw_fused_step_multi")
     return res, int(st.value)
 
@@ -559,6 +615,8 @@ class TensorList:
                                                float(gradient_scale),
                                                0.0 if max_grad_norm is None else float(max_grad_norm),
                                                int(bool(hierarchical)), _stream(self.device), ctypes.byref(res))
+        if rc == RADAMW_ERR_DECISION:
+            raise DecisionMismatch("radamw_list_fused_step", res, step=int(st.value))
         _check(rc, "radamw_list_fused_step")
         return res, int(st.value)
 
@@ -618,6 +676,8 @@ def radamw_lists_fused_step(lists: Sequence[TensorList], steps: Sequence[int], o
         rc = load().radamw_lists_fused_step(handles, k, st, op, float(gradient_scale),
                                             0.0 if max_grad_norm is None else float(max_grad_norm),
                                             int(bool(hierarchical)), _stream(dev), ctypes.byref(res))
+    if rc == RADAMW_ERR_DECISION:
+        raise DecisionMismatch("radamw_lists_fused_step", res, steps=[int(x) for x in st])
     _check(rc, "radamw_lists_fused_step")
     return res, [int(x) for x in st]
 

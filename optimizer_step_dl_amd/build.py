@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libradamw.so")
-SOURCES = ["radamw_api.cpp", "radamw_update.hip", "radamw_stats.hip", "radamw_staged.hip"]
+SOURCES = ["radamw_api.cpp", "radamw_update.hip", "radamw_stats.hip", "radamw_staged.hip", "radamw_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -13,6 +13,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -830,23 +831,23 @@ int decide_host(const radamw_stats *host_report, double gradient_scale, double m
 
 // The host's decision from the report it read, which must be the device's:
 // the same skip, and the same FP32 unscale factor for an update.  Fills the
-// result; *updated tells whether the queued kernels wrote anything.
+// result from the report, with `updated` from the device's decision (the one
+// the queued kernels applied), and *updated likewise; RADAMW_ERR_DECISION
+// when the two decisions differ.
 int settle(const radamw_stats &host, const Decision &dev_dec, double gradient_scale, double max_grad_norm,
            radamw_fused_result *result, bool *updated) {
     radamw_control ctrl;
     int rc = decide_host(&host, gradient_scale, max_grad_norm, &ctrl, result);
     if (rc) return rc;
     const bool skip = ctrl.skip_update != 0;
+    const bool dev_skip = dev_dec.skip != 0;
     const float inv = static_cast<float>(1.0 / ctrl.gradient_scale);
     uint32_t a, b;
     std::memcpy(&a, &inv, 4);
     std::memcpy(&b, &dev_dec.inv_scale, 4);
-    if (skip != (dev_dec.skip != 0) || (!skip && a != b)) {
-        g_last_hip = static_cast<int>(hipErrorUnknown);  // a library fault: the two decisions must agree
-        return RADAMW_ERR_HIP;
-    }
-    result->updated = skip ? 0 : 1;
-    *updated = !skip;
+    result->updated = dev_skip ? 0 : 1;
+    *updated = !dev_skip;
+    if (skip != dev_skip || (!skip && a != b)) return RADAMW_ERR_DECISION;
     return RADAMW_OK;
 }
 
@@ -1092,6 +1093,41 @@ int radamw_step_staged_inplace(float *p, const void *g, radamw_dtype gdt, int64_
     return RADAMW_OK;
 }
 
+int radamw_stream_probe(const float *const *in, int32_t nreads, float *const *out, int32_t nwrites,
+                        int64_t n, int32_t cap_per_cu, radamw_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (nreads < 0 || nreads > 5 || nwrites < 0 || nwrites > 4 || nreads + nwrites < 1) return RADAMW_ERR_INVALID;
+    if (cap_per_cu < 0 || cap_per_cu > MAX_WAVES_PER_CU || n < 0) return RADAMW_ERR_INVALID;
+    if ((nreads > 0 && !in) || !out) return RADAMW_ERR_INVALID;
+    if (n > MAX_ELEMENTS) return RADAMW_ERR_RANGE;
+    if (n % 4 != 0) return RADAMW_ERR_ALIGN;
+    if (n == 0) return RADAMW_OK;
+    if ((n / 4 + 63) / 64 > UPDATE_MAX_GRID) return RADAMW_ERR_RANGE;
+    int dev, rc;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    PtrChecker pc(dev);
+    std::vector<Range> ranges;
+    ProbeArgs a{};
+    for (int32_t r = 0; r < nreads; ++r) {
+        if ((rc = pc.check(in[r], 16, n * 4))) return rc;
+        add_range(ranges, in[r], n * 4, false);
+        a.in[r] = in[r];
+    }
+    for (int32_t w = 0; w < std::max(nwrites, 1); ++w) {
+        if ((rc = pc.check(out[w], 16, n * 4))) return rc;
+        add_range(ranges, out[w], n * 4, true);
+        a.out[w] = out[w];
+    }
+    if ((rc = check_alias(ranges))) return rc;
+    a.chunks = n / 4;
+    a.sink_key = std::numeric_limits<float>::quiet_NaN();
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    rc = hip_status(launch_stream_probe(a, nreads, nwrites, cap_per_cu, stream, timing.start, timing.stop));
+    if (rc == RADAMW_OK) g_launches.fetch_add(1, std::memory_order_relaxed);
+    return rc;
+}
+
 int radamw_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, uint64_t *step,
                       const radamw_options *opts, const radamw_control *ctrl,
                       radamw_stream_t stream_, int32_t *updated) {
@@ -1223,6 +1259,16 @@ int radamw_decide(const radamw_stats *host_report, double gradient_scale, double
     return decide_host(host_report, gradient_scale, max_grad_norm, ctrl, result);
 }
 
+int radamw_check_decision(const radamw_stats *host_report, const uint32_t *device_decision,
+                          double gradient_scale, double max_grad_norm, radamw_fused_result *result) {
+    if (!host_report || !device_decision || !result) return RADAMW_ERR_INVALID;
+    Decision d;
+    d.skip = device_decision[0];
+    std::memcpy(&d.inv_scale, &device_decision[1], 4);
+    bool updated = false;
+    return settle(*host_report, d, gradient_scale, max_grad_norm, result, &updated);
+}
+
 int64_t radamw_fused_workspace_bytes(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt) {
     if (nseg < 0 || (nseg > 0 && !segs) || !valid_dtype(gdt)) return RADAMW_ERR_INVALID;
     int64_t rows = 0;
@@ -1324,9 +1370,10 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
         });
     if (rc) return rc;
     bool updated = false;
-    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated);
+    if (rc != RADAMW_OK && rc != RADAMW_ERR_DECISION) return rc;
     if (updated) *step += 1;
-    return RADAMW_OK;
+    return rc;
 }
 
 int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, int32_t amsgrad,
@@ -1460,9 +1507,10 @@ int radamw_list_fused_step(radamw_list list, uint64_t *step, const radamw_option
         });
     if (rc) return rc;
     bool updated = false;
-    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated);
+    if (rc != RADAMW_OK && rc != RADAMW_ERR_DECISION) return rc;
     if (updated) *step += 1;
-    return RADAMW_OK;
+    return rc;
 }
 
 int radamw_lists_fused_step(const radamw_list *lists, int32_t nlists, uint64_t *steps,
@@ -1554,10 +1602,11 @@ int radamw_lists_fused_step(const radamw_list *lists, int32_t nlists, uint64_t *
         });
     if (rc) return rc;
     bool updated = false;
-    if ((rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated))) return rc;
+    rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated);
+    if (rc != RADAMW_OK && rc != RADAMW_ERR_DECISION) return rc;
     if (updated)
         for (int32_t k : act) steps[k] += 1;
-    return RADAMW_OK;
+    return rc;
 }
 
 int radamw_list_destroy(radamw_list list) {
@@ -1587,6 +1636,7 @@ const char *radamw_status_string(int status) {
     case RADAMW_ERR_ALIGN: return "misaligned pointer";
     case RADAMW_ERR_RANGE: return "size or capacity out of range";
     case RADAMW_ERR_HIP: return "HIP runtime error";
+    case RADAMW_ERR_DECISION: return "host and device decisions differ (the device's was applied)";
     default: return "unknown status";
     }
 }

@@ -40,7 +40,10 @@ constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 // applied by reserving LDS at launch that the kernels never touch.
 constexpr int64_t LDS_PER_CU = 160 * 1024;
 constexpr int MAX_WAVES_PER_CU = 32;
-constexpr int64_t UPDATE_CU_INFLIGHT_BYTES = 72 * 1024;
+#ifndef RADAMW_CU_INFLIGHT_KIB
+#define RADAMW_CU_INFLIGHT_KIB 72
+#endif
+constexpr int64_t UPDATE_CU_INFLIGHT_BYTES = int64_t(RADAMW_CU_INFLIGHT_KIB) * 1024;
 
 // Dynamic LDS that, together with a kernel's `static_bytes` of static LDS,
 // lets exactly `cap` workgroups reside on one CU: the total is the largest
@@ -225,6 +228,20 @@ struct StatsSeg {
     int32_t head;
     int32_t rows;
 };
+
+// The streaming probe (measurement only): nr FP32 read streams and nw write
+// streams of `chunks` 16-byte chunks each; out[0] is the sink of a
+// read-only probe, stored to only where a sum equals sink_key (a NaN).
+struct ProbeArgs {
+    const float *in[5];
+    float *out[4];
+    int64_t chunks;
+    float sink_key;
+};
+// cap_per_cu: resident workgroups per CU (1..32), or 0 for the update's rule
+// (about UPDATE_CU_INFLIGHT_BYTES of tile traffic per CU).
+hipError_t launch_stream_probe(const ProbeArgs &a, int nr, int nw, int cap_per_cu, hipStream_t stream,
+                               hipEvent_t start, hipEvent_t stop);
 
 // The staged (unfused) baseline: 4 launches (5 with vmax != null); *launched
 // receives how many were submitted.

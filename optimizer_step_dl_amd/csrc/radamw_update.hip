@@ -39,6 +39,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #ifndef RADAMW_NT_STORES
 #define RADAMW_NT_STORES 1
 #endif
+// 1: a workgroup reads the fused step's decision before it issues any tile
+// load, so a skipped step moves no tile data; 0: after (the loads' latency
+// then hides the decision's).
+#ifndef RADAMW_DECISION_FIRST
+#define RADAMW_DECISION_FIRST 0
+#endif
 
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
@@ -189,6 +195,9 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
         }
     };
 
+#if RADAMW_DECISION_FIRST
+    if (read_decision(dec, c)) return;
+#endif
     if (base + UPDATE_TILE_CHUNKS <= body) {
         f32x4 P[U], G[U], M[U], V[U], X[U];
 #pragma unroll
@@ -204,8 +213,10 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
                 M[u] = f32x4(0.0f); V[u] = f32x4(0.0f); X[u] = f32x4(0.0f);
             }
         }
+#if !RADAMW_DECISION_FIRST
         loads_issued();
         if (read_decision(dec, c)) return;
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = base + int64_t(u) * UPDATE_BLOCK + tid;
@@ -217,7 +228,9 @@ __device__ __forceinline__ void vector_tile(const SegDesc &s, int64_t tile, cons
             if constexpr (AMS) stream_store(x_out + k, X[u]);
         }
     } else {
+#if !RADAMW_DECISION_FIRST
         if (read_decision(dec, c)) return;
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = base + int64_t(u) * UPDATE_BLOCK + tid;

@@ -175,10 +175,19 @@ class FusedAdamW(torch.optim.Optimizer):
         if self.fused_step:
             # statistics of every active gradient -> one 12-byte report ->
             # one decision for all buckets -> each bucket's update
-            res, steps = _abi.radamw_lists_fused_step(
-                [lst for lst, _, _ in lists], [members[0][1]["step"] for _, _, members in lists],
-                [self._options(group) for _, group, _ in lists], gradient_scale, self.max_grad_norm,
-                self.hierarchical_stats)
+            try:
+                res, steps = _abi.radamw_lists_fused_step(
+                    [lst for lst, _, _ in lists], [members[0][1]["step"] for _, _, members in lists],
+                    [self._options(group) for _, group, _ in lists], gradient_scale, self.max_grad_norm,
+                    self.hierarchical_stats)
+            except _abi.DecisionMismatch as e:
+                # the step ran as the device decided: keep the step counts
+                # consistent with the state it wrote, then report the fault
+                self.last_result = e.result
+                for (_, _, members), new_step in zip(lists, e.steps):
+                    for _, st in members:
+                        st["step"] = new_step
+                raise
             self.last_result = res
         else:
             ctrl = _abi.control(gradient_scale, False)

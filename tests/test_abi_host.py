@@ -233,6 +233,55 @@ def test_list_entry_points_validate_before_any_device_call(lib):
     assert ra.radamw_launch_count() == before
 
 
+def test_check_decision_flags_any_disagreement(lib):
+    """The fused steps' check of the device's decision against the host's
+    (host only): agreement is exact, and every forged disagreement returns
+    RADAMW_ERR_DECISION with ``updated`` following the device, which is the
+    decision the queued kernels applied."""
+    sumsq = 9.0e4  # norm 300 at scale 1: clip = 1 / (300 + 1e-6)
+    rep = _stats(sumsq, 0)
+    ctrl, want = ra.radamw_decide(rep, 1.0, 1.0)
+    inv_bits = int(np.float32(1.0 / ctrl.gradient_scale).view(np.uint32))
+    ok, res = ra.radamw_check_decision(rep, 0, inv_bits, 1.0, 1.0)
+    assert ok and res.updated == 1 and res.clip_coef == want.clip_coef and res.sumsq == sumsq
+    ok, res = ra.radamw_check_decision(rep, 1, inv_bits, 1.0, 1.0)  # device skipped a clean step
+    assert not ok and res.updated == 0 and res.found_inf == 0
+    ok, res = ra.radamw_check_decision(rep, 0, inv_bits + 1, 1.0, 1.0)  # one FP32 ulp of unscale factor
+    assert not ok and res.updated == 1
+    bad = _stats(sumsq, 3)  # the host skips
+    ok, res = ra.radamw_check_decision(bad, 1, 0x7fc00000, 1.0, 1.0)  # a skip ignores the factor
+    assert ok and res.updated == 0 and res.found_inf == 1 and res.nonfinite == 3
+    ok, res = ra.radamw_check_decision(bad, 0, inv_bits, 1.0, 1.0)  # device updated a step with inf
+    assert not ok and res.updated == 1 and res.found_inf == 1
+    dec = (ctypes.c_uint32 * 2)(0, inv_bits)
+    assert lib.radamw_check_decision(None, dec, 1.0, 1.0, ctypes.byref(_abi.FusedResult())) == -1
+    assert lib.radamw_check_decision(ctypes.byref(rep), None, 1.0, 1.0, ctypes.byref(_abi.FusedResult())) == -1
+    assert lib.radamw_check_decision(ctypes.byref(rep), dec, 1.0, 1.0, None) == -1
+    assert lib.radamw_check_decision(ctypes.byref(rep), dec, 0.0, 1.0, ctypes.byref(_abi.FusedResult())) == -1
+    assert ra.radamw_status_string(-7).startswith("host and device decisions differ")
+
+
+def test_stream_probe_validates_before_any_device_call(lib):
+    """The streaming probe's counts, cap and element count are checked
+    before any pointer or device is looked at."""
+    before = ra.radamw_launch_count()
+    fake = (ctypes.c_void_p * 5)(*([0x1000] * 5))
+    call = lambda nr, nw, n=1024, cap=0, ins=fake, outs=fake: lib.radamw_stream_probe(ins, nr, outs, nw, n, cap, None)
+    assert call(6, 1) == -1          # more than 5 read streams
+    assert call(1, 5) == -1          # more than 4 write streams
+    assert call(0, 0) == -1          # no stream at all
+    assert call(-1, 1) == -1
+    assert call(1, 1, cap=33) == -1  # cap above 32 workgroups per CU
+    assert call(1, 1, cap=-1) == -1
+    assert call(1, 1, n=-4) == -1
+    assert call(1, 1, ins=None) == -1
+    assert call(1, 0, outs=None) == -1  # a read-only probe still needs its sink
+    assert call(1, 1, n=1022) == -4  # not a whole number of 16-byte chunks
+    assert call(1, 1, n=(1 << 48) + 4) == -5
+    assert call(1, 1, n=0) == 0      # empty: nothing to launch
+    assert ra.radamw_launch_count() == before
+
+
 def test_lists_fused_step_validates_before_any_device_call(lib):
     """The multi-list fused step rejects a bad array before it reads any
     handle: a handle given twice is caught before it is dereferenced."""

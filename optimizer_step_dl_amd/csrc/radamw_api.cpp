@@ -481,6 +481,36 @@ std::vector<SegDesc> inplace_descs(const radamw_segment *segs, int32_t nseg, voi
     return active;
 }
 
+// Consecutive tensors of a list that continue one another in every stream
+// -- views of one arena per stream, in order -- become one segment: the
+// update is elementwise, so the merged segment computes exactly what its
+// parts would, in one launch instead of one per part (a list of views of a
+// flattened bucket then launches like the bucket itself).
+std::vector<SegDesc> coalesce(const std::vector<SegDesc> &active, int gdt) {
+    std::vector<SegDesc> out;
+    out.reserve(active.size());
+    const int64_t gb = static_cast<int64_t>(grad_bytes(gdt));
+    auto follows = [](const void *next, const void *cur, int64_t bytes) {
+        return reinterpret_cast<uintptr_t>(next) == reinterpret_cast<uintptr_t>(cur) + static_cast<uintptr_t>(bytes);
+    };
+    for (const SegDesc &d : active) {
+        if (!out.empty()) {
+            SegDesc &c = out.back();
+            const int64_t fb = c.n * 4;
+            bool adj = follows(d.p_out, c.p_out, fb) && follows(d.g, c.g, c.n * gb) && follows(d.m_out, c.m_out, fb) &&
+                       follows(d.v_out, c.v_out, fb) && (d.vmax_out == nullptr) == (c.vmax_out == nullptr) &&
+                       (d.vmax_out == nullptr || follows(d.vmax_out, c.vmax_out, fb)) && d.model_kind == c.model_kind &&
+                       (d.model_kind == 0 || follows(d.model, c.model, c.n * 2));
+            if (adj) {
+                c.n += d.n;
+                continue;
+            }
+        }
+        out.push_back(d);
+    }
+    return out;
+}
+
 // Launch policy: a tensor of at least MULTI_SOLO_MIN elements gets a launch
 // of its own; all smaller tensors share one launch.
 void split_launches(const std::vector<SegDesc> &active, std::vector<SegDesc> &solo, std::vector<SegDesc> &shared) {
@@ -570,7 +600,7 @@ int submit_updates(const std::vector<SegDesc> &solo, std::vector<SegDesc> &share
 int multi_update(const radamw_segment *segs, int32_t nseg, int gdt, uint64_t *step,
                  const radamw_options &o, double gradient_scale, int dev, hipStream_t stream,
                  int32_t *updated, void *const *models = nullptr, int model_dtype = 0) {
-    std::vector<SegDesc> active = inplace_descs(segs, nseg, models, model_dtype);
+    std::vector<SegDesc> active = coalesce(inplace_descs(segs, nseg, models, model_dtype), gdt);
     if (active.empty()) {
         *updated = 0;
         return RADAMW_OK;
@@ -1353,7 +1383,7 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
     const int64_t dec_off = (need - 12) % 8 == 0 ? need - 12 : need - 8;
     Decision *dec_dev = reinterpret_cast<Decision *>(static_cast<char *>(workspace) + dec_off);
     std::vector<SegDesc> solo, shared;
-    split_launches(inplace_descs(segs, nseg, nullptr, 0), solo, shared);
+    split_launches(coalesce(inplace_descs(segs, nseg, nullptr, 0), gdt), solo, shared);
     const Coefs c = make_coefs(*opts, *step + 1, gradient_scale);
     const UpdateTiming timing = g_timing;
     g_timing = UpdateTiming{};
@@ -1397,7 +1427,7 @@ int radamw_list_create(const radamw_segment *segs, int32_t nseg, radamw_dtype gd
     l->gdt = gdt;
     l->amsgrad = amsgrad != 0;
     l->active = active;
-    std::vector<SegDesc> descs = inplace_descs(segs, nseg, models, model_dtype);
+    std::vector<SegDesc> descs = coalesce(inplace_descs(segs, nseg, models, model_dtype), gdt);
     split_launches(descs, l->solo, l->shared);
     // heads of an in-place update do not depend on the step, so one table
     // serves the first step and every later one

@@ -374,6 +374,63 @@ def test_random_lists_match_per_tensor_launches(seed, gdt, amsgrad):
             _compare_state(s.param, st, refs[i][0], refs[i][1], amsgrad, what, one_step=True)
 
 
+def test_adjacent_views_of_one_arena_share_one_launch():
+    """Tensors that continue one another in every stream (views of one arena
+    per stream, in order) are updated as one segment: three tensors of at
+    least 2^22 elements take one launch instead of three, bit for bit what
+    per-tensor launches give, and every element matches the oracle.  A gap in
+    any one stream, or the views out of order, split the list there."""
+    sizes = [1 << 22, (1 << 22) + 4, (1 << 22) + 1]
+    total = sum(sizes)
+    announce("adjacent views coalesce")
+    opts = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=True)
+    p0 = synth.normal(total, 0.02, (0, "coalesce", "p")).to(DEV)
+    g0 = synth.stored_grad(total, 1e-3, 1.0, "bf16", (0, "coalesce", "g")).to(DEV)
+    m0, v0, x0 = synth.steady_state(total, (0, "coalesce"), True, DEV)
+
+    def views(gap_in_v=0):
+        arenas = [p0.clone(), g0, m0.clone(), torch.zeros(total + gap_in_v, device=DEV), x0.clone()]
+        segs, off = [], 0
+        for i, n in enumerate(sizes):
+            voff = off + (gap_in_v if i >= 2 else 0)
+            arenas[3][voff:voff + n] = v0[off:off + n]
+            segs.append(ra.Segment(arenas[0][off:off + n], arenas[1][off:off + n], arenas[2][off:off + n],
+                                   arenas[3][voff:voff + n], arenas[4][off:off + n]))
+            off += n
+        return segs
+
+    twins = views()
+    for tw in twins:
+        assert ra.radamw_step_inplace(tw.param, tw.grad, ra.AdamWState(9, tw.exp_avg, tw.exp_avg_sq, tw.max_exp_avg_sq),
+                                      opts, ra.control())
+    for gap, order, launches_expected in ((0, 1, 1), (4, 1, 2), (0, -1, 3)):
+        segs = views(gap)
+        pres = [clone_state(s.param, ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)) for s in segs]
+        before = ra.radamw_launch_count()
+        updated, step = ra.radamw_step_multi(segs[::order], 9, opts, ra.control())
+        assert updated and step == 10
+        assert ra.radamw_launch_count() - before == launches_expected, (gap, order)
+        torch.cuda.synchronize()
+        for i, (s, tw, pre) in enumerate(zip(segs, twins, pres)):
+            for a, b in ((s.param, tw.param), (s.exp_avg, tw.exp_avg), (s.exp_avg_sq, tw.exp_avg_sq),
+                         (s.max_exp_avg_sq, tw.max_exp_avg_sq)):
+                assert bits_equal(a, b), (gap, order, i)
+            if gap == 0 and order == 1:
+                check_step_from(pre, (s.param, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq), s.grad, "bf16", opts,
+                                1.0, 9, f"coalesced view {i}")
+    # a persistent list of the views launches the same way
+    segs = views()
+    lst = ra.TensorList(segs, True)
+    torch.cuda.synchronize()
+    before = ra.radamw_launch_count()
+    updated, step = lst.step(9, opts, ra.control())
+    torch.cuda.synchronize()
+    assert updated and ra.radamw_launch_count() - before == 1
+    for s, tw in zip(segs, twins):
+        assert bits_equal(s.param, tw.param) and bits_equal(s.max_exp_avg_sq, tw.max_exp_avg_sq)
+    lst.close()
+
+
 def test_multi_all_empty_launches_nothing():
     segs = [ra.Segment(torch.empty(0, device=DEV), torch.empty(0, device=DEV), torch.empty(0, device=DEV),
                        torch.empty(0, device=DEV))] * 3

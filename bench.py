@@ -330,7 +330,8 @@ def main(argv=None):
                      "kernel": "adamw_update_single<f32, adamw, steady>",
                      "algorithmic_bytes_per_launch": bpp * n,
                      "stream_ceiling_gbs": ceil_gbs, "frac_of_stream_ceiling": achieved / ceil_gbs,
-                     "stream_ceiling_kernel": "stream_probe<4, 3> (4-read / 3-write, the update's geometry)"},
+                     "stream_ceiling_kernel": "stream_probe<4, 3> (4-read / 3-write, the update's geometry), best "
+                                              "over per-CU caps"},
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_all,
         "kernels": kernels,
@@ -355,36 +356,44 @@ STREAM_PATTERNS = (("read_only_1r", 1, 0), ("write_only_1w", 0, 1), ("copy_1r1w"
                    ("first_step_2r3w", 2, 3), ("adamw_4r3w", 4, 3), ("amsgrad_5r4w", 5, 4))
 
 
-def bench_stream_ceiling(torch, ra, dev, stream, n, reps=20):
+CEILING_CAPS = (0, 8, 9, 10, 11, 12, 14, 16, 32)  # 0: the update kernels' own occupancy rule
+
+
+def bench_stream_ceiling(torch, ra, dev, stream, n, reps=10):
     """radamw_stream_probe over n-element FP32 streams, each a separate
-    allocation like the bucket's: the update kernel's geometry, cache hints
-    and occupancy rule with one add per stream instead of the optimizer's
-    arithmetic.  The 4-read / 3-write pattern is the AdamW update's, 5 / 4
-    AMSGrad's, 2 / 3 a first step's.  Kernel start / end events per launch,
-    averaged over `reps` launches."""
+    allocation like the bucket's: the update kernel's geometry and cache
+    hints with one add per stream instead of the optimizer's arithmetic.
+    The 4-read / 3-write pattern is the AdamW update's, 5 / 4 AMSGrad's,
+    2 / 3 a first step's.  Each pattern runs at the update's occupancy rule
+    and at fixed caps of 8-32 resident workgroups per CU; its ceiling is the
+    best of them.  Kernel start / end events per launch, averaged over
+    `reps` launches."""
     ins = [torch.full((n,), 1.0 + k, dtype=torch.float32, device=dev) for k in range(5)]
     outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(4)]
     out = {}
     for name, nr, nw in STREAM_PATTERNS:
-        args = (ins[:nr], outs[:nw], 0, outs[0] if nw == 0 else None)
-        for _ in range(3):
-            ra.radamw_stream_probe(*args)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
-            a.record(stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        for a, b in ev:
-            ra.radamw_time_next_update(a, b)
-            ra.radamw_stream_probe(*args)
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in ev)
-        avg = sum(ms) / len(ms)
-        nbytes = 4 * (nr + nw) * n
-        out[name] = {"reads": nr, "writes": nw, "bytes_per_element": 4 * (nr + nw), "avg_ms": avg,
-                     "min_ms": ms[0], "gbs": nbytes / (avg * 1e-3) / 1e9}
-        log(f"stream ceiling {name}: {avg:.4f} ms, {out[name]['gbs']:.0f} GB/s")
+        per_cap = {}
+        for cap in CEILING_CAPS:
+            args = (ins[:nr], outs[:nw], cap, outs[0] if nw == 0 else None)
+            for _ in range(2):
+                ra.radamw_stream_probe(*args)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in ev:
+                a.record(stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            for a, b in ev:
+                ra.radamw_time_next_update(a, b)
+                ra.radamw_stream_probe(*args)
+            torch.cuda.synchronize()
+            avg = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+            per_cap["rule" if cap == 0 else str(cap)] = 4 * (nr + nw) * n / (avg * 1e-3) / 1e9
+        best = max(per_cap, key=per_cap.get)
+        out[name] = {"reads": nr, "writes": nw, "bytes_per_element": 4 * (nr + nw), "gbs": per_cap[best],
+                     "best_cap": best, "gbs_at_update_rule": per_cap["rule"],
+                     "gbs_by_cap": {k: round(v, 1) for k, v in per_cap.items()}}
+        log(f"stream ceiling {name}: {per_cap[best]:.0f} GB/s (cap {best}; {per_cap['rule']:.0f} at the update's rule)")
     del ins, outs
     torch.cuda.empty_cache()
     return out

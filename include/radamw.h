@@ -410,6 +410,31 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
                             radamw_stream_t stream, radamw_fused_result *result);
 
 /*
+ * The fused step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * radamw_fused_step_multi over ONE flattened bucket (nseg <= 1; more is
+ * RADAMW_ERR_RANGE) with no workspace argument: the statistics rows, merge
+ * scratch, decision slot and report live in a static device array of the
+ * library (98,560 bytes per device, held until the process ends), which fits
+ * every bucket the library accepts (a tensor writes at most 8192 statistics
+ * rows).  The call allocates no device or pinned host memory (its host-side
+ * validation uses small host containers); on its first call on a device it
+ * looks up that device's copy of the array.  Same arguments, checks,
+ * arithmetic and results as radamw_fused_step_multi, bit for bit; the update
+ * is one launch on `stream`.  The report and the device's decision are read
+ * back behind the update, so the call returns when the step has completed
+ * on the GPU.  Calls on one device share the array and are serialised by a
+ * lock inside the library; work of another process has its own copy.
+ * Nothing in the array needs clearing between calls: every call writes the
+ * rows, records and report it reads.
+ */
+int radamw_fused_step_multi_noalloc(const radamw_segment *segs, int32_t nseg,
+                                    radamw_dtype gdt, uint64_t *step,
+                                    const radamw_options *opts, double gradient_scale,
+                                    double max_grad_norm, int32_t hierarchical,
+                                    radamw_stream_t stream, radamw_fused_result *result);
+
+/*
  * Persistent tensor lists.  A training run updates the same tensors step
  * after step, and validating a list of a few hundred separately allocated
  * tensors (two HIP pointer queries per allocation, the overlap sweep)

@@ -164,6 +164,8 @@ def load(path: str = LIB_PATH):
         "radamw_fused_workspace_bytes": ([P(_Segment), i32, i32], i64),
         "radamw_fused_step_multi": ([P(_Segment), i32, i32, P(u64), P(Options), dbl, dbl, i32, vp, i64, vp,
                                      P(FusedResult)], ctypes.c_int),
+        "radamw_fused_step_multi_noalloc": ([P(_Segment), i32, i32, P(u64), P(Options), dbl, dbl, i32, vp,
+                                             P(FusedResult)], ctypes.c_int),
         "radamw_host_coefficients": ([P(Options), u64, dbl, P(ctypes.c_float)], ctypes.c_int),
         "radamw_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "radamw_last_hip_error": ([], ctypes.c_int),
@@ -188,7 +190,7 @@ EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "rada
            "radamw_step_staged_inplace", "radamw_stream_probe", "radamw_step_multi_writeback",
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_check_decision", "radamw_fused_workspace_bytes",
-           "radamw_fused_step_multi", "radamw_host_coefficients", "radamw_status_string",
+           "radamw_fused_step_multi", "radamw_fused_step_multi_noalloc", "radamw_host_coefficients", "radamw_status_string",
            "radamw_last_hip_error", "radamw_launch_count", "radamw_time_next_update",
            "radamw_list_create", "radamw_list_step", "radamw_list_fused_step", "radamw_list_destroy",
            "radamw_lists_fused_step")
@@ -560,6 +562,27 @@ def radamw_fused_step_multi(segments, step: int, opts: Options,
     if rc == RADAMW_ERR_DECISION:
         raise DecisionMismatch("radamw_fused_step_multi", res, step=int(st.value))
     _check(rc, "radamw_fused_step_multi")
+    return res, int(st.value)
+
+
+def radamw_fused_step_multi_noalloc(segments, step: int, opts: Options, gradient_scale: float,
+                                    max_grad_norm: Optional[float], hierarchical: bool):
+    """radamw_fused_step_multi over one flattened bucket (at most one
+    segment) with no workspace: the library's static device scratch holds
+    the statistics, so the call allocates nothing.  Returns when the step has
+    completed.  Returns (FusedResult, new_step)."""
+    lib = load()
+    arr, code, dev, count = _marshal(segments)
+    st = ctypes.c_uint64(step)
+    res = FusedResult()
+    with torch.cuda.device(dev):
+        rc = lib.radamw_fused_step_multi_noalloc(
+            arr, count, code, ctypes.byref(st), ctypes.byref(opts), float(gradient_scale),
+            0.0 if max_grad_norm is None else float(max_grad_norm), int(bool(hierarchical)), _stream(dev),
+            ctypes.byref(res))
+    if rc == RADAMW_ERR_DECISION:
+        raise DecisionMismatch("radamw_fused_step_multi_noalloc", res, step=int(st.value))
+    _check(rc, "radamw_fused_step_multi_noalloc")
     return res, int(st.value)
 
 

@@ -78,9 +78,35 @@ struct DeviceCache {
     hipStream_t aux = nullptr;
     hipEvent_t fork = nullptr;
     hipEvent_t join = nullptr;
+    // radamw_fused_step_multi_noalloc: the device address of this device's
+    // copy of `scratch` (found once), and the lock that serialises the
+    // calls sharing it
+    std::mutex noalloc_mu;
+    char *noalloc_scratch = nullptr;
 };
 
 DeviceCache g_devices[MAX_DEVICES];
+
+// ------------------------------------------- allocation-free fused step --
+//
+// radamw_fused_step_multi_noalloc keeps what radamw_fused_step_multi puts in
+// the caller's workspace -- the statistics rows, the merge scratch and the
+// decision slot, laid out exactly as in a workspace -- in this file-scope
+// device array, followed by the 12-byte report and a second copy of the
+// decision, which the host reads back together.  It is sized for the largest
+// single-segment step: a tensor writes at most STATS_ROWS_CAP rows, whose
+// fan-in-1024 merge needs ceil(STATS_ROWS_CAP / 1024) intermediate records.
+constexpr int64_t noalloc_merge_records(int64_t rows) {
+    return rows > MERGE_FAN_IN ? (rows + MERGE_FAN_IN - 1) / MERGE_FAN_IN + noalloc_merge_records(
+                                     (rows + MERGE_FAN_IN - 1) / MERGE_FAN_IN) : 0;
+}
+constexpr int64_t NOALLOC_WORKSPACE_BYTES = STATS_ROWS_CAP * 12 + noalloc_merge_records(STATS_ROWS_CAP) * 12 + 12;
+constexpr int64_t NOALLOC_REPORT_OFF = (NOALLOC_WORKSPACE_BYTES + 15) / 16 * 16;  // report: 12 B
+constexpr int64_t NOALLOC_DEC_COPY_OFF = NOALLOC_REPORT_OFF + 16;                   // decision copy: 8 B
+constexpr int64_t NOALLOC_SCRATCH_BYTES = (NOALLOC_DEC_COPY_OFF + 8 + 255) / 256 * 256;
+static_assert(NOALLOC_SCRATCH_BYTES <= 128 * 1024, "the allocation-free step's scratch stays modest");
+
+static __device__ __align__(256) uint64_t scratch[NOALLOC_SCRATCH_BYTES / 8];
 
 // Temporarily make `dev` the calling thread's current device.
 struct DeviceScope {
@@ -1399,6 +1425,84 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg, radamw_dty
                                   dev, stream, timing);
         });
     if (rc) return rc;
+    bool updated = false;
+    rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated);
+    if (rc != RADAMW_OK && rc != RADAMW_ERR_DECISION) return rc;
+    if (updated) *step += 1;
+    return rc;
+}
+
+int radamw_fused_step_multi_noalloc(const radamw_segment *segs, int32_t nseg, radamw_dtype gdt, uint64_t *step,
+                                    const radamw_options *opts, double gradient_scale, double max_grad_norm,
+                                    int32_t hierarchical, radamw_stream_t stream_, radamw_fused_result *result) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc;
+    if ((rc = check_options(opts))) return rc;
+    if ((rc = check_scale(gradient_scale))) return rc;
+    if (!valid_dtype(gdt) || !step || !result || !is_finite(max_grad_norm)) return RADAMW_ERR_INVALID;
+    if (hierarchical != 0 && hierarchical != 1) return RADAMW_ERR_INVALID;
+    if (nseg < 0 || (nseg > 0 && !segs)) return RADAMW_ERR_INVALID;
+    if (nseg > 1) return RADAMW_ERR_RANGE;  // one flattened bucket at most
+    if (*step == UINT64_MAX) return RADAMW_ERR_STATE;
+    int dev;
+    if ((rc = stream_device(stream, &dev))) return rc;
+    int64_t active = 0;
+    if ((rc = check_segments(segs, nseg, gdt, opts->amsgrad != 0, *step == 0, dev, &active))) return rc;
+    const int64_t need = radamw_fused_workspace_bytes(segs, nseg, gdt);
+    if (need < 0) return static_cast<int>(need);
+    if (need > NOALLOC_WORKSPACE_BYTES) return RADAMW_ERR_RANGE;
+    std::memset(result, 0, sizeof *result);
+    result->clip_coef = 1.0;
+    if (active == 0) return RADAMW_OK;
+
+    DeviceCache &dc = g_devices[dev];
+    std::lock_guard<std::mutex> lock(dc.noalloc_mu);  // held until the step has completed
+    if (!dc.noalloc_scratch) {
+        // set-up, once per device, with that device current: `scratch` names
+        // a host-side stand-in; its device copy lives at this address
+        DeviceScope scope(dev);
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        dc.noalloc_scratch = static_cast<char *>(ptr);
+    }
+    char *ws = dc.noalloc_scratch;
+    const radamw_segment &seg = segs[0];
+    StatsRec *rows = reinterpret_cast<StatsRec *>(ws);
+    const int64_t nrows = stats_rows(seg.n, gdt);
+    rc = hip_status(launch_analyze(seg.grad, gdt, seg.n, stats_head(seg.grad, gdt, seg.n), nrows, rows, stream));
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    const StatsRec *cur = nullptr;
+    int64_t count = 0;
+    if ((rc = merge_levels(rows, nrows, rows + nrows, hierarchical != 0, stream, &cur, &count))) return rc;
+    // the decision slot where a workspace of `need` bytes keeps it
+    const int64_t dec_off = (need - 12) % 8 == 0 ? need - 12 : need - 8;
+    Decision *dec_dev = reinterpret_cast<Decision *>(ws + dec_off);
+    StatsRec *report = reinterpret_cast<StatsRec *>(ws + NOALLOC_REPORT_OFF);
+    Decision *dec_copy = reinterpret_cast<Decision *>(ws + NOALLOC_DEC_COPY_OFF);
+    rc = hip_status(launch_merge_decide(cur, count, report, dec_dev, dec_copy,
+                                        DecideArgs{gradient_scale, max_grad_norm}, stream));
+    if (rc) return rc;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    // one segment: one update launch on `stream` (no second stream, no table)
+    std::vector<SegDesc> solo, shared;
+    split_launches(inplace_descs(segs, nseg, nullptr, 0), solo, shared);
+    const Coefs c = make_coefs(*opts, *step + 1, gradient_scale);
+    const UpdateTiming timing = g_timing;
+    g_timing = UpdateTiming{};
+    if ((rc = submit_updates(solo, shared, nullptr, nullptr, gdt, opts->amsgrad != 0, *step == 0, c, dec_dev, dev,
+                             stream, timing)))
+        return rc;
+    // the report and the device's decision, read back behind the update
+    uint32_t back[6];
+    hipError_t e = hipMemcpyAsync(back, ws + NOALLOC_REPORT_OFF, sizeof back, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    radamw_stats host;
+    std::memcpy(host.w, back, 12);
+    Decision dd;
+    std::memcpy(&dd, back + 4, sizeof dd);
     bool updated = false;
     rc = settle(host, dd, gradient_scale, max_grad_norm, result, &updated);
     if (rc != RADAMW_OK && rc != RADAMW_ERR_DECISION) return rc;

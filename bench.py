@@ -201,7 +201,7 @@ def main(argv=None):
     # ------------------------------------------------ update-only variants --
     wanted = [] if args.variants == "none" else (
         ["adamw_f32_outofplace", "amsgrad_f32_inplace", "amsgrad_f32_outofplace", "adamw_bf16_inplace",
-         "adamw_f32_firststep", "adamw_f32_bf16copy"] if args.variants == "all" else
+         "amsgrad_f16_inplace", "adamw_f32_firststep", "adamw_f32_bf16copy"] if args.variants == "all" else
         [v for v in args.variants.split(",") if v not in ("decoder_1b", "decoder_7b", "staged", "optim_1b")])
     variants = {}
     for name in wanted:

@@ -34,14 +34,17 @@ constexpr int64_t UPDATE_TILE_ELEMS = UPDATE_TILE_CHUNKS * 4;
 // every stream in flight.  That is more than HBM serves best: on MI355X
 // (2^28-element buckets, every update variant: FP32 / 16-bit gradients,
 // AdamW / AMSGrad, steady / first step, with and without a model copy)
-// throughput peaked when a CU held about 72 KiB of tile traffic (reads plus
-// writes), i.e. 8-16 workgroups, at 6.55-6.68 TB/s, against 6.0-6.3 TB/s at
-// full occupancy; fewer than that starved the memory system.  The cap is
-// applied by reserving LDS at launch that the kernels never touch.
+// throughput is highest when a CU holds about 64 KiB of tile traffic (reads
+// plus writes), i.e. 7-14 workgroups, at 6.45-6.76 TB/s depending on the
+// box, against 6.0-6.3 TB/s at full occupancy.  Budgets of 60-72 KiB are
+// within 1% of one another for AdamW; 64 KiB was never worse than 72 KiB
+// on two boxes and up to 1.9% better for AMSGrad and first steps; 56 KiB
+// and below starve the memory system (5.5-6.3 TB/s).  The cap is applied
+// by reserving LDS at launch that the kernels never touch.
 constexpr int64_t LDS_PER_CU = 160 * 1024;
 constexpr int MAX_WAVES_PER_CU = 32;
 #ifndef RADAMW_CU_INFLIGHT_KIB
-#define RADAMW_CU_INFLIGHT_KIB 72
+#define RADAMW_CU_INFLIGHT_KIB 64
 #endif
 constexpr int64_t UPDATE_CU_INFLIGHT_BYTES = int64_t(RADAMW_CU_INFLIGHT_KIB) * 1024;
 

@@ -90,14 +90,51 @@ def counters_from_profile():
         return None
 
 
-def build_inputs(torch, synth, n, variant, gdt, device):
+def time_update(torch, ra, stream, p, g, m, v, vmax, opts, reps=20):
+    """Average of the update kernel's own start / end events over ``reps``
+    in-place launches at t = 1000."""
+    c = ra.control(1.0)
+    for k in range(3):
+        ra.radamw_step_inplace(p, g, ra.AdamWState(999 + k, m, v, vmax), opts, c)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(ev):
+        ra.radamw_time_next_update(a, b)
+        ra.radamw_step_inplace(p, g, ra.AdamWState(999 + k, m, v, vmax), opts, c)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+def build_inputs(torch, synth, ra, n, variant, gdt, device, layout="bucket", outputs=False):
     """Config-3 bucket: p ~ N(0, 0.02), g ~ N(0, 1e-3), m ~ N(0, 1e-4),
-    v = N(0, 1e-3)^2, v_max = v * U(1, 1.5); drawn on the device."""
+    v = N(0, 1e-3)^2, v_max = v * U(1, 1.5); drawn on the device.  layout
+    "bucket": one allocation in the library's stream placement
+    (ra.bucket_arena; with ``outputs`` also the out-of-place outputs p', m',
+    v', v_max'); "separate": one allocation per stream.  Returns (p, g, m, v,
+    v_max or None, outputs or None)."""
     key = (0, "bucket", n)
+    amsgrad = variant == "amsgrad"
     p = synth.normal(n, 0.02, key + ("p",), device)
     g = synth.stored_grad(n, 1e-3, 1.0, gdt, key + ("g",), device)
-    m, v, vmax = synth.steady_state(n, key, variant == "amsgrad", device, m_std=1e-4, v_root_std=1e-3)
-    return p, g, m, v, vmax
+    m, v, vmax = synth.steady_state(n, key, amsgrad, device, m_std=1e-4, v_root_std=1e-3)
+    state = [p, g, m, v] + ([vmax] if amsgrad else [])
+    nout = (4 if amsgrad else 3) if outputs else 0
+    if layout == "separate":
+        outs = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(nout)]
+    else:
+        views = ra.bucket_arena(n, [t.dtype for t in state] + [torch.float32] * nout, device)
+        for dst, src in zip(views, state):
+            dst.copy_(src)
+        state, outs = views[:len(state)], views[len(state):]
+        del p, g, m, v, vmax
+    outs = (outs + [None])[:4] if outputs else None
+    if outs is not None and not amsgrad:
+        outs = outs[:3] + [None]
+    return state[0], state[1], state[2], state[3], (state[4] if amsgrad else None), outs
 
 
 def main(argv=None):
@@ -135,7 +172,7 @@ def main(argv=None):
     smi_before = clock_snapshot(props)
 
     # ---------------------------------------------------- headline step --
-    p, g, m, v, _ = build_inputs(torch, synth, n, "adamw", "f32", dev)
+    p, g, m, v, _, _ = build_inputs(torch, synth, ra, n, "adamw", "f32", dev)
     opts = ra.options(lr=1e-3, weight_decay=1e-4)
     seglist = ra.SegmentList([ra.Segment(p, g, m, v, None)])
     ws = torch.empty(ra.radamw_fused_workspace_bytes(seglist), dtype=torch.uint8, device=dev)
@@ -193,10 +230,21 @@ def main(argv=None):
     del p, g, m, v, ws, seglist
     torch.cuda.empty_cache()
 
+    # the same update over the same recipe in separate allocations (one per
+    # stream), beside the bucket placement the headline uses
+    sep = build_inputs(torch, synth, ra, n, "adamw", "f32", dev, layout="separate")
+    sep_ms = time_update(torch, ra, stream, sep[0], sep[1], sep[2], sep[3], None, ra.options(lr=1e-3, weight_decay=1e-4))
+    sep_gbs = bpp * n / (sep_ms * 1e-3) / 1e9
+    kernels["update_adamw_f32_inplace_separate_allocations"] = {"avg_ms": sep_ms, "gbs": sep_gbs,
+                                                                "frac_of_peak": sep_gbs / HBM_PEAK_GBS}
+    log(f"update in separate allocations: {sep_ms:.3f} ms ({sep_gbs:.0f} GB/s)")
+    del sep
+    torch.cuda.empty_cache()
+
     # ------------------------------------- streaming ceiling of the pattern --
     ceiling = bench_stream_ceiling(torch, ra, dev, stream, n)
-    ceil_gbs = ceiling["adamw_4r3w"]["gbs"]
-    log(f"update / 4-read 3-write ceiling: {achieved / ceil_gbs:.4f}")
+    ceil_gbs = ceiling["adamw_in_place"]["gbs"]
+    log(f"update / ceiling of its own access pattern: {achieved / ceil_gbs:.4f}")
 
     # ------------------------------------------------ update-only variants --
     wanted = [] if args.variants == "none" else (
@@ -208,7 +256,7 @@ def main(argv=None):
         variant, gdt, mode = name.split("_")
         first = mode == "firststep"
         amsgrad = variant == "amsgrad"
-        p, g, m, v, vmax = build_inputs(torch, synth, n, variant, gdt, dev)
+        p, g, m, v, vmax, outs = build_inputs(torch, synth, ra, n, variant, gdt, dev, outputs=mode == "outofplace")
         o = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
         c = ra.control(1.0)
         st_step = 0 if first else 999
@@ -220,8 +268,6 @@ def main(argv=None):
             def launch(k):
                 ra.radamw_step_multi_writeback(seg, [model], st_step + k, o, c)
         elif mode == "outofplace":
-            outs = [torch.empty_like(p), torch.empty_like(m), torch.empty_like(v),
-                    torch.empty_like(vmax) if amsgrad else None]
             sets = [(p, m, v, vmax), tuple(outs)]
 
             def launch(k):
@@ -252,9 +298,9 @@ def main(argv=None):
                           "params_per_s": n / (avg * 1e-3), "gbs": bp * n / (avg * 1e-3) / 1e9,
                           "frac_of_peak": bp * n / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"variant {name}: {avg:.3f} ms, {variants[name]['gbs']:.0f} GB/s")
-        del p, g, m, v, vmax
+        del p, g, m, v, vmax, outs
         if mode == "outofplace":
-            del outs, sets
+            del sets
         torch.cuda.empty_cache()
 
     # ------------------------------- staged baseline A/B (the pages' bench) --
@@ -323,6 +369,7 @@ def main(argv=None):
                          "wd 1e-4, steady state from t=1000, in place; step = grad stats + hierarchical merge + "
                          "12-byte read-back + global-norm clip at 1.0 + fused update"),
             "n_params": n, "grad_dtype": "f32", "optimizer": "adamw", "storage": "in-place",
+            "layout": "p, g, m, v in one allocation placed by radamw_bucket_layout",
             "parallelism": "none (1 GPU)",
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -330,8 +377,10 @@ def main(argv=None):
                      "kernel": "adamw_update_single<f32, adamw, steady>",
                      "algorithmic_bytes_per_launch": bpp * n,
                      "stream_ceiling_gbs": ceil_gbs, "frac_of_stream_ceiling": achieved / ceil_gbs,
-                     "stream_ceiling_kernel": "stream_probe<4, 3> (4-read / 3-write, the update's geometry), best "
-                                              "over per-CU caps"},
+                     "stream_ceiling_kernel": "stream_probe<4, 3> over the update's own streams (4 reads, 3 written "
+                                              "back in place, bucket placement), best over per-CU caps",
+                     "layout": "one allocation, radamw_bucket_layout placement",
+                     "separate_allocations_gbs": sep_gbs},
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_all,
         "kernels": kernels,
@@ -354,47 +403,65 @@ def main(argv=None):
 
 STREAM_PATTERNS = (("read_only_1r", 1, 0), ("write_only_1w", 0, 1), ("copy_1r1w", 1, 1),
                    ("first_step_2r3w", 2, 3), ("adamw_4r3w", 4, 3), ("amsgrad_5r4w", 5, 4))
-
-
 CEILING_CAPS = (0, 8, 9, 10, 11, 12, 14, 16, 32)  # 0: the update kernels' own occupancy rule
 
 
+def _probe_best(torch, ra, stream, ins, outs, sink, n, nbytes, reps):
+    per_cap = {}
+    for cap in CEILING_CAPS:
+        args = (ins, outs, cap, sink)
+        for _ in range(2):
+            ra.radamw_stream_probe(*args)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for a, b in ev:
+            ra.radamw_time_next_update(a, b)
+            ra.radamw_stream_probe(*args)
+        torch.cuda.synchronize()
+        avg = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        per_cap["rule" if cap == 0 else str(cap)] = nbytes * n / (avg * 1e-3) / 1e9
+    best = max(per_cap, key=per_cap.get)
+    return {"gbs": per_cap[best], "best_cap": best, "gbs_at_update_rule": per_cap["rule"],
+            "gbs_by_cap": {k: round(v, 1) for k, v in per_cap.items()}}
+
+
 def bench_stream_ceiling(torch, ra, dev, stream, n, reps=10):
-    """radamw_stream_probe over n-element FP32 streams, each a separate
-    allocation like the bucket's: the update kernel's geometry and cache
-    hints with one add per stream instead of the optimizer's arithmetic.
-    The 4-read / 3-write pattern is the AdamW update's, 5 / 4 AMSGrad's,
-    2 / 3 a first step's.  Each pattern runs at the update's occupancy rule
-    and at fixed caps of 8-32 resident workgroups per CU; its ceiling is the
-    best of them.  Kernel start / end events per launch, averaged over
-    `reps` launches."""
-    ins = [torch.full((n,), 1.0 + k, dtype=torch.float32, device=dev) for k in range(5)]
-    outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(4)]
+    """radamw_stream_probe over n-element FP32 streams: the update kernel's
+    geometry and cache hints with one add per stream instead of the
+    optimizer's arithmetic, each pattern at the update's occupancy rule and
+    at fixed caps of 8-32 resident workgroups per CU, its ceiling the best
+    of them.  "adamw_in_place" is the headline update's own pattern -- four
+    streams in the bucket placement, three of them written back in place --
+    and is the ceiling the roofline is compared with; the other patterns use
+    separate streams in the bucket placement (4 reads / 3 writes is AdamW out
+    of place, 5 / 4 AMSGrad, 2 / 3 a first step), and
+    "adamw_4r3w_separate_allocations" one allocation per stream.  Kernel
+    start / end events per launch, averaged over `reps` launches."""
     out = {}
+    arena = ra.bucket_arena(n, [torch.float32] * 9, dev)
+    for k, t in enumerate(arena):
+        t.fill_(1.0 + k)
+    ins, outs = arena[:5], arena[5:]
+    r = _probe_best(torch, ra, stream, ins[:4], [ins[0], ins[2], ins[3]], None, n, 28, reps)
+    out["adamw_in_place"] = dict(r, reads=4, writes=3, bytes_per_element=28, layout="bucket, in place")
+    log(f"stream ceiling adamw_in_place: {r['gbs']:.0f} GB/s (cap {r['best_cap']}; {r['gbs_at_update_rule']:.0f} "
+        "at the update's rule)")
     for name, nr, nw in STREAM_PATTERNS:
-        per_cap = {}
-        for cap in CEILING_CAPS:
-            args = (ins[:nr], outs[:nw], cap, outs[0] if nw == 0 else None)
-            for _ in range(2):
-                ra.radamw_stream_probe(*args)
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for a, b in ev:
-                a.record(stream)
-                b.record(stream)
-            torch.cuda.synchronize()
-            for a, b in ev:
-                ra.radamw_time_next_update(a, b)
-                ra.radamw_stream_probe(*args)
-            torch.cuda.synchronize()
-            avg = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-            per_cap["rule" if cap == 0 else str(cap)] = 4 * (nr + nw) * n / (avg * 1e-3) / 1e9
-        best = max(per_cap, key=per_cap.get)
-        out[name] = {"reads": nr, "writes": nw, "bytes_per_element": 4 * (nr + nw), "gbs": per_cap[best],
-                     "best_cap": best, "gbs_at_update_rule": per_cap["rule"],
-                     "gbs_by_cap": {k: round(v, 1) for k, v in per_cap.items()}}
-        log(f"stream ceiling {name}: {per_cap[best]:.0f} GB/s (cap {best}; {per_cap['rule']:.0f} at the update's rule)")
-    del ins, outs
+        r = _probe_best(torch, ra, stream, ins[:nr], outs[:nw], outs[0] if nw == 0 else None, n, 4 * (nr + nw), reps)
+        out[name] = dict(r, reads=nr, writes=nw, bytes_per_element=4 * (nr + nw), layout="bucket")
+        log(f"stream ceiling {name}: {r['gbs']:.0f} GB/s (cap {r['best_cap']}; {r['gbs_at_update_rule']:.0f} at the "
+            "update's rule)")
+    del arena, ins, outs
+    torch.cuda.empty_cache()
+    sep = [torch.full((n,), 1.0 + k, dtype=torch.float32, device=dev) for k in range(7)]
+    r = _probe_best(torch, ra, stream, sep[:4], sep[4:], None, n, 28, reps)
+    out["adamw_4r3w_separate_allocations"] = dict(r, reads=4, writes=3, bytes_per_element=28, layout="separate")
+    log(f"stream ceiling adamw_4r3w_separate_allocations: {r['gbs']:.0f} GB/s (cap {r['best_cap']})")
+    del sep
     torch.cuda.empty_cache()
     return out
 
@@ -412,7 +479,7 @@ def bench_staged(torch, synth, ra, dev, stream, n):
     out = {}
     for variant, bpp_f, bpp_s in (("adamw", 28, 48), ("amsgrad", 36, 60)):
         amsgrad = variant == "amsgrad"
-        p, g, m, v, vmax = build_inputs(torch, synth, n, variant, "f32", dev)
+        p, g, m, v, vmax, _ = build_inputs(torch, synth, ra, n, variant, "f32", dev)
         delta = torch.empty_like(p)
         o = ra.options(lr=1e-3, weight_decay=1e-4, amsgrad=amsgrad)
         c = ra.control(1.0)
@@ -616,15 +683,13 @@ def bench_optimizer_1b(torch, synth, ra, dev, stream):
 
 def decoder_1b_flat(torch, synth, ra, dev, shapes, key0):
     """The 1.1B decoder's state as one flattened bucket: p, the FP16
-    gradient, m, v and v_max are each one contiguous allocation of all
-    1,261,529,088 elements, filled tensor by tensor with the list's own draws
-    (FP32 masters N(0, 0.02), FP16 gradients N(0, 1e-4) x 1024, m ~ N(0,
-    1e-5), v = N(0, 1e-4)^2, v_max = v U(1, 1.5)).  Returns the five arenas
-    and each tensor's (offset, size)."""
+    gradient, m, v and v_max of all 1,261,529,088 elements in one allocation
+    placed by radamw_bucket_layout, filled tensor by tensor with the list's
+    own draws (FP32 masters N(0, 0.02), FP16 gradients N(0, 1e-4) x 1024,
+    m ~ N(0, 1e-5), v = N(0, 1e-4)^2, v_max = v U(1, 1.5)).  Returns the five
+    streams and each tensor's (offset, size)."""
     total = synth.total(shapes)
-    arena = [torch.empty(total, dtype=torch.float32, device=dev),
-             torch.empty(total, dtype=torch.float16, device=dev)] + \
-            [torch.empty(total, dtype=torch.float32, device=dev) for _ in range(3)]
+    arena = ra.bucket_arena(total, [torch.float32, torch.float16, torch.float32, torch.float32, torch.float32], dev)
     spans, off = [], 0
     for i, (_, n) in enumerate(shapes):
         key = key0 + (i,)
@@ -645,8 +710,9 @@ def bench_decoder_list(torch, synth, ra, dev, stream):
       multi_list   one radamw_step_multi call over the 201 separately
                    allocated tensors: 156 large tensors launched alone, the
                    45 norm vectors in one shared launch, over two streams;
-      multi_views  the same call over 201 views of one contiguous arena per
-                   stream (the same launch split);
+      multi_views  the same call over 201 views of one arena per stream (in
+                   the bucket placement of radamw_bucket_layout), which the
+                   library merges into one segment: one launch;
       flat_bucket  one radamw_step_multi call over the arena as a single
                    segment: one launch of 1,261,529,088 elements (the pages'
                    pre-flattened bucket, which shares options and step)."""

@@ -152,6 +152,7 @@ def load(path: str = LIB_PATH):
         "radamw_step_staged_inplace": ([vp, vp, i32, i64, P(_State), vp, P(Options), P(Control), vp, P(i32)],
                                        ctypes.c_int),
         "radamw_stream_probe": ([P(vp), i32, P(vp), i32, i64, i32, vp], ctypes.c_int),
+        "radamw_bucket_layout": ([i64, P(i32), i32, P(i64), P(i64)], ctypes.c_int),
         "radamw_step_multi_writeback": ([P(_Segment), P(vp), i32, i32, i32, P(u64), P(Options), P(Control), vp,
                                          P(i32)], ctypes.c_int),
         "radamw_stats_plan": ([i64, P(i64), P(i32)], ctypes.c_int),
@@ -187,7 +188,7 @@ def load(path: str = LIB_PATH):
 
 
 EXPORTS = ("radamw_options_default", "radamw_step", "radamw_step_inplace", "radamw_step_multi",
-           "radamw_step_staged_inplace", "radamw_stream_probe", "radamw_step_multi_writeback",
+           "radamw_step_staged_inplace", "radamw_stream_probe", "radamw_bucket_layout", "radamw_step_multi_writeback",
            "radamw_stats_plan", "radamw_grad_stats_rows", "radamw_grad_stats", "radamw_merge_stats",
            "radamw_read_report", "radamw_decide", "radamw_check_decision", "radamw_fused_workspace_bytes",
            "radamw_fused_step_multi", "radamw_fused_step_multi_noalloc", "radamw_host_coefficients", "radamw_status_string",
@@ -393,6 +394,7 @@ def radamw_stream_probe(ins: Sequence[torch.Tensor], outs: Sequence[torch.Tensor
     n = tensors[0].numel()
     for i, t in enumerate(tensors):
         _dense(t, f"stream {i}", torch.float32, n, dev)
+    # an output given as one of the inputs is updated in place
     if not outs and sink is None:
         raise ValueError("a read-only probe needs a sink tensor")
     pin = (ctypes.c_void_p * max(1, len(ins)))(*[t.data_ptr() for t in ins])
@@ -401,6 +403,41 @@ def radamw_stream_probe(ins: Sequence[torch.Tensor], outs: Sequence[torch.Tensor
     with torch.cuda.device(dev):
         rc = lib.radamw_stream_probe(pin, len(ins), pout, len(outs), n, int(cap_per_cu), _stream(dev))
     _check(rc, "radamw_stream_probe")
+
+
+def radamw_bucket_layout(n: int, element_bytes: Sequence[int]):
+    """(byte offsets, arena bytes) of the library's placement for the
+    streams of one flattened bucket in a single allocation."""
+    k = len(element_bytes)
+    eb = (ctypes.c_int32 * max(1, k))(*[int(x) for x in element_bytes])
+    offs = (ctypes.c_int64 * max(1, k))()
+    total = ctypes.c_int64()
+    _check(load().radamw_bucket_layout(int(n), eb, k, offs, ctypes.byref(total)), "radamw_bucket_layout")
+    return [int(offs[i]) for i in range(k)], int(total.value)
+
+
+_PITCH_ALIGN = 2 << 20
+
+
+def bucket_arena(n: int, dtypes: Sequence[torch.dtype], device=None):
+    """One device allocation holding len(dtypes) streams of n elements, placed
+    by radamw_bucket_layout (from a 2 MiB-aligned start).  Returns the views,
+    in order; each keeps the allocation alive."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    sizes = [torch.empty(0, dtype=d).element_size() for d in dtypes]
+    offs, total = radamw_bucket_layout(n, sizes)
+    raw = torch.empty(total + _PITCH_ALIGN, dtype=torch.uint8, device=device)
+    lead = (-raw.data_ptr()) % _PITCH_ALIGN
+    return [raw[lead + o:lead + o + n * es].view(d) for o, es, d in zip(offs, sizes, dtypes)]
+
+
+def bucket_segment(n: int, grad_dtype: torch.dtype = torch.float32, amsgrad: bool = False, device=None) -> Segment:
+    """A flattened bucket's p, gradient, m, v (and v_max) as one allocation
+    in the library's placement (bucket_arena); contents uninitialised."""
+    f32 = torch.float32
+    dts = [f32, grad_dtype, f32, f32] + ([f32] if amsgrad else [])
+    views = bucket_arena(n, dts, device)
+    return Segment(views[0], views[1], views[2], views[3], views[4] if amsgrad else None)
 
 
 def radamw_step_multi(segments, step: int, opts: Options, ctrl: Control):

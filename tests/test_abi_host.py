@@ -233,6 +233,34 @@ def test_list_entry_points_validate_before_any_device_call(lib):
     assert ra.radamw_launch_count() == before
 
 
+@pytest.mark.parametrize("n,sizes", [(1 << 28, [4, 4, 4, 4]), (1261529088, [4, 2, 4, 4, 4]), (100_000_007, [4, 2]),
+                                     (1, [8]), (0, [4, 4]), (3 * 4096 + 1031, [4, 2, 4, 4, 4, 4, 4, 4, 4])])
+def test_bucket_layout_rule(lib, n, sizes):
+    """Stream k of a bucket starts at k * pitch, pitch = the widest stream
+    rounded up to 2 MiB plus 12 KiB; the streams fit and never overlap."""
+    offs, total = ra.radamw_bucket_layout(n, sizes)
+    widest = n * max(sizes)
+    pitch = -(-widest // (2 << 20)) * (2 << 20) + (12 << 10)
+    assert offs == [k * pitch for k in range(len(sizes))] and total == len(sizes) * pitch
+    for k, es in enumerate(sizes):
+        assert offs[k] % 4096 == 0 and offs[k] + n * es <= (offs[k + 1] if k + 1 < len(sizes) else total)
+
+
+def test_bucket_layout_rejects_bad_arguments(lib):
+    offs = (ctypes.c_int64 * 4)()
+    total = ctypes.c_int64(-9)
+    eb = (ctypes.c_int32 * 4)(4, 4, 4, 4)
+    assert lib.radamw_bucket_layout(16, eb, 0, offs, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout(16, eb, 17, offs, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout(-1, eb, 4, offs, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout(16, None, 4, offs, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout(16, eb, 4, None, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout(16, eb, 4, offs, None) == -1
+    assert lib.radamw_bucket_layout(16, (ctypes.c_int32 * 4)(4, 3, 4, 4), 4, offs, ctypes.byref(total)) == -1
+    assert lib.radamw_bucket_layout((1 << 48) + 1, eb, 4, offs, ctypes.byref(total)) == -5
+    assert total.value == -9
+
+
 def test_check_decision_flags_any_disagreement(lib):
     """The fused steps' check of the device's decision against the host's
     (host only): agreement is exact, and every forged disagreement returns

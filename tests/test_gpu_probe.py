@@ -42,13 +42,33 @@ def test_probe_moves_every_stream(nr, nw, cap):
         assert int(torch.count_nonzero(sink)) == 0
 
 
+def test_probe_in_place_streams():
+    """Outputs that are inputs are updated in place, the update's own
+    pattern: 4 reads, 3 of them written back."""
+    n = 4 * 5003
+    announce("stream probe in place 4r/3w")
+    host = [synth.normal(n, 1.0, (0, "probe-ip", r)) for r in range(4)]
+    ins = [t.to(DEV) for t in host]
+    ra.radamw_stream_probe(ins, [ins[0], ins[2], ins[3]])
+    torch.cuda.synchronize()
+    s = host[0].numpy().copy()
+    for t in host[1:]:
+        s = (s + t.numpy()).astype(np.float32)
+    for w, t in enumerate((ins[0], ins[2], ins[3])):
+        assert np.array_equal(t.cpu().numpy().view(np.uint32), (s + np.float32(w)).astype(np.float32).view(np.uint32))
+    assert np.array_equal(ins[1].cpu().numpy(), host[1].numpy())  # the read-only stream is untouched
+
+
 def test_probe_argument_checks():
     announce("stream probe argument checks")
     n = 1024
     a = [torch.ones(n, device=DEV) for _ in range(3)]
     base = torch.empty(n + 4, device=DEV)
-    with pytest.raises(ra.RadamwError) as e:  # written range overlapping a read range
-        ra.radamw_stream_probe([a[0]], [a[0]])
+    with pytest.raises(ra.RadamwError) as e:  # written range partly overlapping a read range
+        ra.radamw_stream_probe([a[0][4:]], [a[0][:n - 4]])
+    assert e.value.status == -3
+    with pytest.raises(ra.RadamwError) as e:  # the same output twice
+        ra.radamw_stream_probe([a[0]], [a[1], a[1]])
     assert e.value.status == -3
     with pytest.raises(ra.RadamwError) as e:  # not 16-byte aligned
         ra.radamw_stream_probe([a[0]], [base[1:n + 1]])

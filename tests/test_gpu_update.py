@@ -431,6 +431,39 @@ def test_adjacent_views_of_one_arena_share_one_launch():
     lst.close()
 
 
+@pytest.mark.parametrize("gdt,amsgrad", [("f32", False), ("bf16", True)])
+def test_bucket_arena_layout_changes_nothing_but_placement(gdt, amsgrad):
+    """A flattened bucket allocated by bucket_segment (one allocation, the
+    library's stream placement) is updated exactly like the same bucket in
+    separate allocations, bit for bit, and every element matches the
+    oracle; its streams sit where radamw_bucket_layout puts them."""
+    n = 3 * 4096 + 1031
+    announce(f"bucket arena {gdt} ams={amsgrad}")
+    seg = ra.bucket_segment(n, TORCH_GDT[gdt], amsgrad, DEV)
+    sizes = [4, 4 if gdt == "f32" else 2, 4, 4] + ([4] if amsgrad else [])
+    offs, _ = ra.radamw_bucket_layout(n, sizes)
+    ptrs = [t.data_ptr() for t in (seg.param, seg.grad, seg.exp_avg, seg.exp_avg_sq, seg.max_exp_avg_sq) if t is not None]
+    assert [q - ptrs[0] for q in ptrs] == offs and ptrs[0] % (2 << 20) == 0
+    seg.param.copy_(synth.normal(n, 0.02, (0, "arena", gdt, "p")).to(DEV))
+    seg.grad.copy_(synth.stored_grad(n, 1e-3, 1.0, gdt, (0, "arena", gdt, "g")).to(DEV))
+    m, v, x = synth.steady_state(n, (0, "arena", gdt), amsgrad, DEV)
+    seg.exp_avg.copy_(m)
+    seg.exp_avg_sq.copy_(v)
+    if amsgrad:
+        seg.max_exp_avg_sq.copy_(x)
+    twin = ra.Segment(seg.param.clone(), seg.grad.clone(), m.clone(), v.clone(), None if x is None else x.clone())
+    opts = ra.options(lr=1e-3, weight_decay=0.01, amsgrad=amsgrad)
+    pre = clone_state(seg.param, ra.AdamWState(0, seg.exp_avg, seg.exp_avg_sq, seg.max_exp_avg_sq))
+    assert ra.radamw_step_multi([seg], 41, opts, ra.control())[0]
+    assert ra.radamw_step_multi([twin], 41, opts, ra.control())[0]
+    torch.cuda.synchronize()
+    for a, b in ((seg.param, twin.param), (seg.exp_avg, twin.exp_avg), (seg.exp_avg_sq, twin.exp_avg_sq),
+                 (seg.max_exp_avg_sq, twin.max_exp_avg_sq)):
+        assert (a is None and b is None) or bits_equal(a, b)
+    check_step_from(pre, (seg.param, seg.exp_avg, seg.exp_avg_sq, seg.max_exp_avg_sq), seg.grad, gdt, opts, 1.0, 41,
+                    "bucket arena")
+
+
 def test_multi_all_empty_launches_nothing():
     segs = [ra.Segment(torch.empty(0, device=DEV), torch.empty(0, device=DEV), torch.empty(0, device=DEV),
                        torch.empty(0, device=DEV))] * 3

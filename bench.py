@@ -676,7 +676,28 @@ def bench_optimizer_1b(torch, synth, ra, dev, stream):
            "python_overhead_ms": ms - c_ms, "clip_coef": res.clip_coef if res else None}
     log(f"FusedAdamW 1.1B fused step: {ms:.3f} ms ({out['params_per_s']:.3g} params/s), the C call alone "
         f"{c_ms:.3f} ms, {len(tlists)} launch bucket(s)")
-    del opt, params, lists, tlists
+    del opt, lists, tlists
+    torch.cuda.empty_cache()
+    # the same parameters and gradients under flatten=True: one bucket
+    # allocation in the library's placement, one analysis and one update
+    # launch per step
+    opt = FusedAdamW(params, lr=1e-3, weight_decay=1e-4, fused_step=True, max_grad_norm=1.0,
+                     hierarchical_stats=True, flatten=True)
+    for _ in range(3):
+        opt.step()
+    torch.cuda.synchronize()
+    launches = ra.radamw_launch_count()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        opt.step()
+    torch.cuda.synchronize()
+    fms = (time.perf_counter() - t0) * 1e3 / steps
+    out["flatten"] = {"step_ms": fms, "params_per_s": n_total / (fms * 1e-3),
+                      "launches_per_step": (ra.radamw_launch_count() - launches) / steps,
+                      "gbs_at_28_bytes_per_param": 28 * n_total / (fms * 1e-3) / 1e9}
+    log(f"FusedAdamW 1.1B fused step, flatten=True: {fms:.3f} ms ({out['flatten']['params_per_s']:.3g} params/s, "
+        f"{out['flatten']['launches_per_step']:.0f} launches per step)")
+    del opt, params
     torch.cuda.empty_cache()
     return out
 

@@ -222,3 +222,175 @@ def test_bucket_lists_reused_while_storage_unchanged():
     assert len(opt._cache) == 1
     torch.cuda.synchronize()
     assert [opt.state[p]["step"] for p in params] == [4, 4, 3, 3]
+
+
+# ---------------------------------------------------------- flatten=True --
+
+def _flat_pair(key, **kw):
+    """Two copies of the same model: one under FusedAdamW(flatten=True), one
+    under the default per-tensor FusedAdamW, with the same options."""
+    pa = _model(key)
+    pb = [torch.nn.Parameter(p.detach().clone()) for p in pa]
+    opt_a = FusedAdamW(_groups(pa), flatten=True, **kw)
+    opt_b = FusedAdamW(_groups(pb), **kw)
+    return pa, pb, opt_a, opt_b
+
+
+def _same(a, b):
+    return torch.equal(a.detach().view(torch.int32), b.detach().view(torch.int32))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_flatten_equals_per_tensor_steps(fused):
+    """flatten=True puts each group's parameters, gradients and moments in
+    one bucket allocation (views of it) and steps it as one segment; without
+    clipping the results are those of per-tensor steps bit for bit (the
+    update is elementwise), and every state tensor is a view of the bucket."""
+    announce(f"FusedAdamW flatten fused={fused}")
+    key = (0, "optflat", fused)
+    pa, pb, opt_a, opt_b = _flat_pair(key, fused_step=fused)
+    for b in opt_a._flat:
+        arena = b["streams"]
+        base = arena[0].data_ptr()
+        assert base % (2 << 20) == 0
+        for p, off, n in b["members"]:
+            assert p.data_ptr() == base + 4 * off and p.grad.data_ptr() == arena[1].data_ptr() + 4 * off
+            assert opt_a.state[p]["exp_avg"].data_ptr() == arena[2].data_ptr() + 4 * off
+    for t in range(1, 5):
+        for i, (a, b) in enumerate(zip(pa, pb)):
+            g = synth.stored_grad(a.numel(), 1e-3, 1.0, "f32", key + (i, "g", t)).to(DEV)
+            a.grad.copy_(g)
+            b.grad = g.clone()
+        launches = ra.radamw_launch_count()
+        opt_a.step()
+        if not fused:
+            assert ra.radamw_launch_count() - launches == 2  # one update launch per group
+        opt_b.step()
+        torch.cuda.synchronize()
+        for a, b in zip(pa, pb):
+            assert _same(a, b)
+            for name in ("exp_avg", "exp_avg_sq"):
+                assert _same(opt_a.state[a][name], opt_b.state[b][name])
+            assert opt_a.state[a]["step"] == opt_b.state[b]["step"] == t
+
+
+def test_flatten_clip_matches_oracle_and_skips():
+    """Fused step with clipping over flattened groups: each step matches the
+    oracle at the clip the step reported; a NaN skips the whole step."""
+    announce("FusedAdamW flatten clip")
+    params = _model((0, "optflc"))
+    mirror = OracleMirror(params, _groups(params))
+    opt = FusedAdamW(_groups(params), fused_step=True, max_grad_norm=0.05, hierarchical_stats=True, flatten=True)
+    for t in range(1, 5):
+        grads = []
+        for i, p in enumerate(params):
+            g = synth.stored_grad(p.numel(), 1e-3, 256.0, "f32", (0, "optflc", i, "g", t)).to(DEV)
+            if t == 3 and i == 2:
+                g[123] = float("nan")
+            p.grad.copy_(g)
+            grads.append(g)
+        opt.step(gradient_scale=256.0)
+        torch.cuda.synchronize()
+        res = opt.last_result
+        skip, eff = oracle.decide(res.sumsq, res.nonfinite, 256.0, 0.05)
+        assert bool(res.found_inf) == skip == (t == 3)
+        mirror.step(grads, scale=eff, skip=skip)
+        for i, p in enumerate(params):
+            contract_one_step(host(p), mirror.p[i], f"flat param {i} step {t}")
+            assert opt.state[p]["step"] == mirror.st[i].step
+
+
+def test_flatten_backward_accumulates_into_the_bucket():
+    """A small model trained with loss.backward(): the gradients land in the
+    bucket (autograd accumulates into the existing .grad in place),
+    zero_grad() zeroes them there, and the weights follow the per-tensor
+    optimizer bit for bit."""
+    announce("FusedAdamW flatten with autograd")
+    torch.manual_seed(0)
+    ma = torch.nn.Sequential(torch.nn.Linear(64, 128), torch.nn.ReLU(), torch.nn.Linear(128, 10)).to(DEV)
+    mb = torch.nn.Sequential(torch.nn.Linear(64, 128), torch.nn.ReLU(), torch.nn.Linear(128, 10)).to(DEV)
+    mb.load_state_dict(ma.state_dict())
+    opt_a = FusedAdamW(ma.parameters(), lr=1e-2, weight_decay=0.01, flatten=True)
+    opt_b = FusedAdamW(mb.parameters(), lr=1e-2, weight_decay=0.01)
+    g_arena = opt_a._flat[0]["streams"][1]
+    for t in range(5):
+        x = synth.normal(32 * 64, 1.0, (0, "optfla", t, "x")).view(32, 64).to(DEV)
+        y = torch.arange(32, device=DEV) % 10
+        for m, o in ((ma, opt_a), (mb, opt_b)):
+            o.zero_grad()
+            torch.nn.functional.cross_entropy(m(x), y).backward()
+            o.step()
+        for p in ma.parameters():
+            lo = g_arena.data_ptr()
+            assert lo <= p.grad.data_ptr() < lo + g_arena.numel() * 4
+        torch.cuda.synchronize()
+        for a, b in zip(ma.parameters(), mb.parameters()):
+            assert _same(a, b), t
+    opt_a.zero_grad()
+    assert int(torch.count_nonzero(g_arena)) == 0
+    assert all(p.grad is not None for p in ma.parameters())
+
+
+def test_flatten_state_dict_is_compact_and_resumes_bit_exact():
+    """state_dict() of a flattened optimizer stores compact copies of each
+    parameter's state (not the bucket behind the views); loading it puts
+    the state back into the bucket, and the resumed run equals the
+    uninterrupted one bit for bit."""
+    announce("FusedAdamW flatten resume")
+    key = (0, "optflr")
+    pa = _model(key)
+    opt_a = FusedAdamW(_groups(pa), fused_step=True, flatten=True)
+    for t in range(1, 4):
+        for i, p in enumerate(pa):
+            p.grad.copy_(synth.stored_grad(p.numel(), 1e-3, 1.0, "f32", key + (i, "g", t)).to(DEV))
+        opt_a.step()
+    buf = io.BytesIO()
+    torch.save({"params": [p.detach().clone() for p in pa], "opt": opt_a.state_dict()}, buf)
+    assert buf.tell() < 3 * 4 * sum(SIZES) + (1 << 20)  # p, m, v once each (+ v_max of one group), no bucket
+    for t in range(4, 7):
+        for i, p in enumerate(pa):
+            p.grad.copy_(synth.stored_grad(p.numel(), 1e-3, 1.0, "f32", key + (i, "g", t)).to(DEV))
+        opt_a.step()
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    pb = [torch.nn.Parameter(x.to(DEV)) for x in ck["params"]]
+    opt_b = FusedAdamW(_groups(pb), flatten=True)
+    opt_b.load_state_dict(ck["opt"])
+    arena = opt_b._flat[0]["streams"]
+    assert opt_b.state[pb[0]]["exp_avg"].data_ptr() == arena[2].data_ptr()
+    for t in range(4, 7):
+        for i, p in enumerate(pb):
+            p.grad.copy_(synth.stored_grad(p.numel(), 1e-3, 1.0, "f32", key + (i, "g", t)).to(DEV))
+        opt_b.step()
+    torch.cuda.synchronize()
+    for a, b in zip(pa, pb):
+        assert _same(a, b) and _same(opt_a.state[a]["exp_avg_sq"], opt_b.state[b]["exp_avg_sq"])
+
+
+def test_flatten_sixteen_bit_gradients_and_replaced_grad():
+    """A BF16 gradient bucket under FP32 masters; a .grad replaced by a new
+    tensor is copied back into the bucket before the step; the result
+    matches the oracle."""
+    announce("FusedAdamW flatten bf16 grads")
+    params = _model((0, "optflb"))
+    ref = [host(p) for p in params]
+    states = [oracle.State(p.numel(), False) for p in params]
+    oo = oracle.Options(lr=1e-3, weight_decay=0.01)
+    opt = FusedAdamW(params, lr=1e-3, weight_decay=0.01, flatten=True, flatten_grad_dtype=torch.bfloat16)
+    assert opt._flat[0]["streams"][1].dtype == torch.bfloat16
+    for t in range(1, 4):
+        grads = []
+        for i, p in enumerate(params):
+            g = synth.stored_grad(p.numel(), 1e-3, 1.0, "bf16", (0, "optflb", i, "g", t)).to(DEV)
+            if i == 1 and t == 2:
+                p.grad = g.clone()  # a new tensor: copied back into the bucket
+            else:
+                p.grad.copy_(g)
+            grads.append(grad_host(g))
+        opt.step()
+        torch.cuda.synchronize()
+        for i, g in enumerate(grads):
+            oracle.adamw_step(ref[i], g, "bf16", states[i], oo, 1.0)
+            contract_one_step(host(params[i]), ref[i], f"flat bf16 param {i} step {t}")
+    g_arena = opt._flat[0]["streams"][1]
+    assert params[1].grad.data_ptr() == g_arena.data_ptr() + 2 * SIZES[0]

@@ -47,3 +47,8 @@ def test_step_options_versions_and_old_archives():
     bad["step_options"] = dict(bad["step_options"], version=9)
     with pytest.raises(ValueError):
         target.load_state_dict(bad)
+
+
+def test_flatten_needs_device_parameters():
+    with pytest.raises(ValueError):
+        FusedAdamW(_params(), flatten=True)  # CPU parameters

@@ -573,9 +573,11 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
     (BF16 grads N(0,1e-4), in-place AdamW, steady state at t = 11):
     statistics of all gradients (13.5 GB read), hierarchical merge, 12-byte
     read-back, clip at 1.0, update (227 launches: 226 large tensors alone,
-    the 65 norm vectors in one).  Timed twice: one radamw_fused_step_multi
-    call per step (every call validates 1164 buffers), then the same steps
-    through a persistent tensor list (validated once)."""
+    the 65 norm vectors in one).  Timed three ways: one
+    radamw_fused_step_multi call per step (every call validates 1164
+    buffers), the same steps through a persistent tensor list (validated
+    once), and the same parameters as one flattened bucket in the library's
+    placement (one analysis and one update launch)."""
     shapes = synth.decoder_7b_shapes()
     total = synth.total(shapes)
     segs = []
@@ -624,7 +626,34 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
     log(f"decoder 6.7B fused step (list): {ms:.2f} ms ({out['params_per_s']:.3g} params/s), update {ums:.2f} ms "
         f"({out['update_gbs']:.0f} GB/s), stats + read-back {ms - ums:.2f} ms; per call {ms_call:.2f} ms; "
         f"clip {res.clip_coef:.4f}")
-    del seglist, segs, ws
+    del seglist, segs, ws, lst
+    torch.cuda.empty_cache()
+    # the same parameters as one flattened bucket: p, the BF16 gradient, m
+    # and v each one stream of all 6.7e9 elements, in one allocation placed
+    # by radamw_bucket_layout, filled tensor by tensor with the same draws
+    arena = ra.bucket_arena(total, [torch.float32, torch.bfloat16, torch.float32, torch.float32], dev)
+    off = 0
+    for i, (_, n) in enumerate(shapes):
+        key = (0, "dec7b-bench", i)
+        arena[0][off:off + n] = synth.normal(n, 0.02, key + ("p",), dev)
+        arena[1][off:off + n] = synth.stored_grad(n, 1e-4, 1.0, "bf16", key + ("g",), dev)
+        m, v, _ = synth.steady_state(n, key, False, dev, m_std=1e-5, v_root_std=1e-4)
+        arena[2][off:off + n], arena[3][off:off + n] = m, v
+        off += n
+    del m, v
+    flat = ra.TensorList([ra.Segment(*arena)], False)
+    flat_step = lambda st: flat.fused_step(st, opts, 1.0, 1.0, True)
+    res, step = flat_step(step)  # warm
+    torch.cuda.synchronize()
+    fms, fums, res, step = timed(flat_step, step)
+    flat.close()
+    out["flat_bucket"] = {"path": "radamw_list_fused_step over one segment in the bucket placement",
+                          "step_ms_median": fms, "params_per_s": total / (fms * 1e-3), "update_ms_median": fums,
+                          "update_gbs": 26 * total / (fums * 1e-3) / 1e9, "stats_and_decision_ms": fms - fums,
+                          "clip_coef": res.clip_coef}
+    log(f"decoder 6.7B fused step (one flattened bucket): {fms:.2f} ms ({total / (fms * 1e-3):.3g} params/s), update "
+        f"{fums:.2f} ms ({out['flat_bucket']['update_gbs']:.0f} GB/s), stats + read-back {fms - fums:.2f} ms")
+    del arena
     torch.cuda.empty_cache()
     return out
 

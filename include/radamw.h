@@ -221,9 +221,11 @@ int radamw_step_inplace(float *p, const void *g, radamw_dtype gdt, int64_t n,
  * update at ~6.44-6.55 TB/s, in separate allocations at ~6.54-6.59 TB/s,
  * and back to back in one allocation with each stream's start shifted by a
  * further 12 KiB at ~6.76-6.83 TB/s (3-4.5% faster for AdamW, AMSGrad and
- * 16-bit gradients; 1.8-3.6% at 1.26e9 and 1e8+7 elements).  The rule is
- * measured, not derived: stream k starts at byte offset k * pitch, with
- * pitch = (n * max element size rounded up to 2 MiB) + 12 KiB.
+ * 16-bit gradients; 3.6% at 1e8+7 elements).  The gain is for streams up to
+ * about 1 GiB: streams of 5-27 GB came within +-2% of separate allocations.
+ * The rule is measured, not derived: stream k starts at byte offset
+ * k * pitch, with pitch = (n * max element size rounded up to 2 MiB) +
+ * 12 KiB.
  *   n              : elements of every stream (0 <= n <= 2^48).
  *   element_bytes  : host array of nstreams element sizes (1, 2, 4 or 8),
  *                    in the order the caller wants the streams placed

@@ -168,9 +168,11 @@ size_t grad_bytes(int gdt) { return gdt == RADAMW_F32 ? 4 : 2; }
 // starts at k * pitch in one allocation, pitch = its largest stream rounded
 // up to 2 MiB plus 12 KiB.  Measured on MI355X: streams whose starts differ
 // by exact multiples of large powers of two (1 GiB apart, or separately
-// allocated 2 MiB-aligned buffers) update 3-4.5% slower than streams whose
-// starts are further shifted by 4-20 KiB or 1 MiB; 12 KiB was best or
-// within noise of the best for every variant and size swept.
+// allocated 2 MiB-aligned buffers) update 3-6% slower than streams whose
+// starts are further shifted by 4-20 KiB or 1 MiB, for streams of up to
+// about 1 GiB; 12 KiB was best or within noise of the best for every
+// variant swept.  Streams of 5-27 GB came within +-2% of separate
+// allocations either way.
 constexpr int64_t BUCKET_PITCH_ALIGN = int64_t(2) << 20;
 constexpr int64_t BUCKET_STREAM_SHIFT = int64_t(12) << 10;
 

@@ -11,8 +11,8 @@ import torch
 import oracle
 import synth
 import optimizer_step_dl_amd as ra
-from gpu_helpers import (DEV, TORCH_GDT, announce, bits_equal, contract_one_step, grad_host, host,
-                         new_gpu_state, normwise, oracle_opts)
+from gpu_helpers import (DEV, TORCH_GDT, announce, bits_equal, check_step_from, clone_state, contract_one_step,
+                         grad_host, host, new_gpu_state, normwise, oracle_opts)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,19 @@ def _fill_grads(segs, twins, sizes, gdt, scale, key, t):
         tw.grad.copy_(s.grad)
 
 
+def _pre(segs):
+    return [clone_state(s.param, ra.AdamWState(0, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq)) for s in segs]
+
+
+def _one_step_checks(segs, pres, sizes, gdt, opts, scale, step_before, what):
+    """Every element of every non-empty segment against the oracle run one
+    update from the segment's own pre-step state (contract + moment ulps)."""
+    for i, (s, pre) in enumerate(zip(segs, pres)):
+        if sizes[i]:
+            check_step_from(pre, (s.param, s.exp_avg, s.exp_avg_sq, s.max_exp_avg_sq), s.grad, gdt, opts, scale,
+                            step_before, f"{what} segment {i} n={sizes[i]}")
+
+
 def _same_bits(a: ra.Segment, b: ra.Segment, amsgrad: bool, what: str):
     assert bits_equal(a.param, b.param), f"{what}: param"
     assert bits_equal(a.exp_avg, b.exp_avg), f"{what}: exp_avg"
@@ -72,12 +85,14 @@ def test_list_step_matches_step_multi_and_oracle(gdt, amsgrad):
             for i, s in enumerate(segs):
                 if SIZES[i]:
                     oracle.adamw_step(refs[i][0], grad_host(s.grad), gdt, refs[i][1], oracle_opts(opts), scale)
+            pres = _pre(segs)
             before = ra.radamw_launch_count()
             updated, step = lst.step(step, opts, ra.control(scale))
             assert updated and step == t
             assert ra.radamw_launch_count() - before == solo + 1  # no table staging: launches only
             _, tstep = ra.radamw_step_multi(twins, tstep, opts, ra.control(scale))
             torch.cuda.synchronize()
+            _one_step_checks(segs, pres, SIZES, gdt, opts, scale, t - 1, f"list step {t}")
             for i, (s, tw) in enumerate(zip(segs, twins)):
                 _same_bits(s, tw, amsgrad, f"step {t} segment {i} n={SIZES[i]}")
                 if t == 1 and SIZES[i]:
@@ -120,9 +135,13 @@ def test_list_fused_step_matches_fused_multi_and_oracle():
                     acc.add(grad_host(s.grad), gdt)
                 skip_ref, eff_ref = oracle.decide(*acc.result, 1.0, max_norm)
                 assert not skip_ref
+            pres, step_before = _pre(segs), step
             res, step = lst.fused_step(step, opts, 1.0, max_norm, True)
             tres, tstep = ra.radamw_fused_step_multi(twins, tstep, opts, 1.0, max_norm, True, ws)
             torch.cuda.synchronize()
+            if res.updated:  # one update at the clip the report decided
+                _, eff = oracle.decide(res.sumsq, res.nonfinite, 1.0, max_norm)
+                _one_step_checks(segs, pres, SIZES, gdt, opts, eff, step_before, f"fused step {t}")
             assert (res.sumsq, res.nonfinite, res.found_inf, res.updated, res.clip_coef, res.total_norm) == \
                 (tres.sumsq, tres.nonfinite, tres.found_inf, tres.updated, tres.clip_coef, tres.total_norm)
             assert step == tstep
@@ -255,8 +274,13 @@ def test_lists_fused_step_two_groups_match_oracle():
                 acc.add(grad_host(g), gdt)
             sumsq, count = acc.result
             skip, eff = oracle.decide(sumsq, count, scale, max_norm)
+            pres = [_pre(segs) for segs, _, _, _ in groups]
             res, new_steps = ra.radamw_lists_fused_step([la, lb], steps, [opts_a, opts_b], scale, max_norm, True)
             torch.cuda.synchronize()
+            if res.updated:  # each group one update from its own state, at the decided clip
+                _, eff_dev = oracle.decide(res.sumsq, res.nonfinite, scale, max_norm)
+                for (segs, _, sizes, opts), pre, st in zip(groups, pres, steps):
+                    _one_step_checks(segs, pre, sizes, gdt, opts, eff_dev, st, f"lists step {t}")
             assert bool(res.found_inf) == skip == (t == 2) and res.nonfinite == count
             assert abs(res.sumsq - sumsq) <= (sum(sizes_a + sizes_b) * 2.0**-53 + 1e-12) * sumsq
             if skip:

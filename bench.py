@@ -24,7 +24,8 @@ sysfs), "provenance" (command line, commit, source and library hashes),
 "staged_vs_fused" (the pages' staged baseline A/B), "decoder_1b_list"
 (per-tensor launches, the multi-tensor call over the list, and one
 flattened bucket), "decoder_7b_fused_step" (the whole step over a
-6.7B-parameter list), "fusedadamw_1b" (the torch optimizer),
+6.7B-parameter list and as one bucket, with the streaming ceiling at that
+stream length), "fusedadamw_1b" (the torch optimizer),
 "copy_calibration" (torch's copy kernel used to scale the HBM counters).
 """
 from __future__ import annotations
@@ -577,7 +578,9 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
     radamw_fused_step_multi call per step (every call validates 1164
     buffers), the same steps through a persistent tensor list (validated
     once), and the same parameters as one flattened bucket in the library's
-    placement (one analysis and one update launch)."""
+    placement (one analysis and one update launch).  Then the streaming
+    probe over FP32 streams of the same element count, the ceiling at this
+    stream length."""
     shapes = synth.decoder_7b_shapes()
     total = synth.total(shapes)
     segs = []
@@ -655,6 +658,22 @@ def bench_decoder_7b(torch, synth, ra, dev, stream):
         f"{fums:.2f} ms ({out['flat_bucket']['update_gbs']:.0f} GB/s), stats + read-back {fms - fums:.2f} ms")
     del arena
     torch.cuda.empty_cache()
+    # the streaming ceiling at this size: what the memory system gives the
+    # update's geometry falls with the stream length, so the update is also
+    # compared with the probe over streams of the same element count
+    probe = ra.bucket_arena(total, [torch.float32] * 4, dev)
+    for k, t in enumerate(probe):
+        t.fill_(1.0 + k)
+    r = _probe_best(torch, ra, stream, probe, [probe[0], probe[2], probe[3]], None, total, 28, 3)
+    del probe
+    torch.cuda.empty_cache()
+    out["stream_ceiling"] = dict(
+        r, kernel="stream_probe<4, 3>",
+        what="4 FP32 streams of the same element count in the bucket placement, 3 written back in place "
+             "(28 B/element; the update's BF16 gradient stream moves 2 B/element)",
+        list_update_frac=out["update_gbs"] / r["gbs"], flat_update_frac=out["flat_bucket"]["update_gbs"] / r["gbs"])
+    log(f"decoder 6.7B stream ceiling (same element count): {r['gbs']:.0f} GB/s (cap {r['best_cap']}); update "
+        f"{out['update_gbs'] / r['gbs']:.3f} (list), {out['flat_bucket']['update_gbs'] / r['gbs']:.3f} (flat) of it")
     return out
 
 

@@ -298,6 +298,10 @@ def main(argv=None):
         variants[name] = {"avg_ms": avg, "min_ms": min(ms), "bytes_per_param": bp,
                           "params_per_s": n / (avg * 1e-3), "gbs": bp * n / (avg * 1e-3) / 1e9,
                           "frac_of_peak": bp * n / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        pattern = VARIANT_CEILING.get(name)
+        if pattern in ceiling:
+            variants[name].update(stream_ceiling_pattern=pattern,
+                                  frac_of_stream_ceiling=variants[name]["gbs"] / ceiling[pattern]["gbs"])
         log(f"variant {name}: {avg:.3f} ms, {variants[name]['gbs']:.0f} GB/s")
         del p, g, m, v, vmax, outs
         if mode == "outofplace":
@@ -405,6 +409,10 @@ def main(argv=None):
 STREAM_PATTERNS = (("read_only_1r", 1, 0), ("write_only_1w", 0, 1), ("copy_1r1w", 1, 1),
                    ("first_step_2r3w", 2, 3), ("adamw_4r3w", 4, 3), ("amsgrad_5r4w", 5, 4))
 CEILING_CAPS = (0, 8, 9, 10, 11, 12, 14, 16, 32)  # 0: the update kernels' own occupancy rule
+# the probe pattern that moves each FP32-gradient variant's streams (a
+# 16-bit gradient or model-copy stream has no FP32 probe pattern)
+VARIANT_CEILING = {"adamw_f32_outofplace": "adamw_4r3w", "amsgrad_f32_inplace": "amsgrad_in_place",
+                   "amsgrad_f32_outofplace": "amsgrad_5r4w", "adamw_f32_firststep": "first_step_in_place"}
 
 
 def _probe_best(torch, ra, stream, ins, outs, sink, n, nbytes, reps):
@@ -437,7 +445,10 @@ def bench_stream_ceiling(torch, ra, dev, stream, n, reps=10):
     at fixed caps of 8-32 resident workgroups per CU, its ceiling the best
     of them.  "adamw_in_place" is the headline update's own pattern -- four
     streams in the bucket placement, three of them written back in place --
-    and is the ceiling the roofline is compared with; the other patterns use
+    and is the ceiling the roofline is compared with; "amsgrad_in_place"
+    (five streams, four written back) and "first_step_in_place" (p and g
+    read, p written back, m and v written) are the other in-place updates'
+    patterns; the other patterns use
     separate streams in the bucket placement (4 reads / 3 writes is AdamW out
     of place, 5 / 4 AMSGrad, 2 / 3 a first step), and
     "adamw_4r3w_separate_allocations" one allocation per stream.  Kernel
@@ -447,10 +458,16 @@ def bench_stream_ceiling(torch, ra, dev, stream, n, reps=10):
     for k, t in enumerate(arena):
         t.fill_(1.0 + k)
     ins, outs = arena[:5], arena[5:]
-    r = _probe_best(torch, ra, stream, ins[:4], [ins[0], ins[2], ins[3]], None, n, 28, reps)
-    out["adamw_in_place"] = dict(r, reads=4, writes=3, bytes_per_element=28, layout="bucket, in place")
-    log(f"stream ceiling adamw_in_place: {r['gbs']:.0f} GB/s (cap {r['best_cap']}; {r['gbs_at_update_rule']:.0f} "
-        "at the update's rule)")
+    # the in-place updates' own patterns: p, g, m, v (, v_max) read and all
+    # but g written back; a first step reads p and g and writes p, m, v
+    in_place = (("adamw_in_place", ins[:4], [ins[0], ins[2], ins[3]], 28),
+                ("amsgrad_in_place", ins[:5], [ins[0], ins[2], ins[3], ins[4]], 36),
+                ("first_step_in_place", ins[:2], [ins[0], ins[2], ins[3]], 20))
+    for name, rd, wr, nbytes in in_place:
+        r = _probe_best(torch, ra, stream, rd, wr, None, n, nbytes, reps)
+        out[name] = dict(r, reads=len(rd), writes=len(wr), bytes_per_element=nbytes, layout="bucket, in place")
+        log(f"stream ceiling {name}: {r['gbs']:.0f} GB/s (cap {r['best_cap']}; {r['gbs_at_update_rule']:.0f} "
+            "at the update's rule)")
     for name, nr, nw in STREAM_PATTERNS:
         r = _probe_best(torch, ra, stream, ins[:nr], outs[:nw], outs[0] if nw == 0 else None, n, 4 * (nr + nw), reps)
         out[name] = dict(r, reads=nr, writes=nw, bytes_per_element=4 * (nr + nw), layout="bucket")

@@ -105,7 +105,7 @@ class FusedAdamW(torch.optim.Optimizer):
         """Move each parameter group into one bucket allocation (see the
         module docstring): parameters, gradients and moments become views."""
         f32 = torch.float32
-        for group in self.param_groups:
+        for gi, group in enumerate(self.param_groups):
             params = list(group["params"])
             if not params:
                 continue
@@ -152,7 +152,9 @@ class FusedAdamW(torch.optim.Optimizer):
                     members.append((p, off, n))
                     self._flat_ids.add(id(p))
                     off += n
-            self._flat.append({"group": group, "amsgrad": ams, "grad_dtype": gd, "streams": streams,
+            # the group is found by its index at every step: load_state_dict
+            # replaces the group dicts, and schedulers edit the current ones
+            self._flat.append({"group_index": gi, "amsgrad": ams, "grad_dtype": gd, "streams": streams,
                                "members": members, "list": None})
 
     def _flat_lists(self):
@@ -162,7 +164,8 @@ class FusedAdamW(torch.optim.Optimizer):
         single-segment persistent list."""
         out = []
         for b in self._flat:
-            if bool(b["group"]["amsgrad"]) != b["amsgrad"]:
+            group = self.param_groups[b["group_index"]]
+            if bool(group["amsgrad"]) != b["amsgrad"]:
                 raise RuntimeError("amsgrad of a flattened group cannot change")
             g_arena = b["streams"][1]
             with torch.no_grad():
@@ -179,7 +182,7 @@ class FusedAdamW(torch.optim.Optimizer):
                 raise RuntimeError("the parameters of a flattened group share one step count")
             if b["list"] is None:
                 b["list"] = _abi.TensorList([_abi.Segment(*b["streams"])], b["amsgrad"])
-            out.append((b["list"], b["group"], [(p, self.state[p]) for p, _, _ in b["members"]]))
+            out.append((b["list"], group, [(p, self.state[p]) for p, _, _ in b["members"]]))
         return out
 
     @torch.no_grad()

@@ -367,6 +367,42 @@ def test_flatten_state_dict_is_compact_and_resumes_bit_exact():
         assert _same(a, b) and _same(opt_a.state[a]["exp_avg_sq"], opt_b.state[b]["exp_avg_sq"])
 
 
+def test_flatten_follows_group_options_after_load():
+    """load_state_dict replaces the parameter-group dicts.  A flattened group
+    then steps with the options of the current dicts, the ones an LR
+    scheduler edits: bit for bit the per-tensor optimizer under the same
+    edits (with the options held before the load, lr and weight decay would
+    differ)."""
+    announce("FusedAdamW flatten options after load")
+    key = (0, "optflo")
+    pa, pb, opt_a, opt_b = _flat_pair(key)
+
+    def set_grads(t):
+        for i, (a, b) in enumerate(zip(pa, pb)):
+            g = synth.stored_grad(a.numel(), 1e-3, 1.0, "f32", key + (i, "g", t)).to(DEV)
+            a.grad.copy_(g)
+            b.grad = g.clone()
+
+    for t in (1, 2):
+        set_grads(t)
+        opt_a.step()
+        opt_b.step()
+    for o in (opt_a, opt_b):
+        o.load_state_dict(o.state_dict())
+        o.param_groups[0]["lr"] = 3e-3
+        o.param_groups[1]["weight_decay"] = 0.0
+    for t in (3, 4):
+        set_grads(t)
+        opt_a.step()
+        opt_b.step()
+    torch.cuda.synchronize()
+    for a, b in zip(pa, pb):
+        assert _same(a, b)
+        for name in ("exp_avg", "exp_avg_sq"):
+            assert _same(opt_a.state[a][name], opt_b.state[b][name])
+        assert opt_a.state[a]["step"] == opt_b.state[b]["step"] == 4
+
+
 def test_flatten_sixteen_bit_gradients_and_replaced_grad():
     """A BF16 gradient bucket under FP32 masters; a .grad replaced by a new
     tensor is copied back into the bucket before the step; the result

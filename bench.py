@@ -408,7 +408,7 @@ def main(argv=None):
 
 STREAM_PATTERNS = (("read_only_1r", 1, 0), ("write_only_1w", 0, 1), ("copy_1r1w", 1, 1),
                    ("first_step_2r3w", 2, 3), ("adamw_4r3w", 4, 3), ("amsgrad_5r4w", 5, 4))
-CEILING_CAPS = (0, 8, 9, 10, 11, 12, 14, 16, 32)  # 0: the update kernels' own occupancy rule
+CEILING_CAPS = (0, 4, 5, 6, 7, 8, 9, 10, 11, 12, 14, 16, 32)  # 0: the update kernels' own occupancy rule
 # the probe pattern that moves each FP32-gradient variant's streams (a
 # 16-bit gradient or model-copy stream has no FP32 probe pattern)
 VARIANT_CEILING = {"adamw_f32_outofplace": "adamw_4r3w", "amsgrad_f32_inplace": "amsgrad_in_place",
@@ -442,7 +442,7 @@ def bench_stream_ceiling(torch, ra, dev, stream, n, reps=10):
     """radamw_stream_probe over n-element FP32 streams: the update kernel's
     geometry and cache hints with one add per stream instead of the
     optimizer's arithmetic, each pattern at the update's occupancy rule and
-    at fixed caps of 8-32 resident workgroups per CU, its ceiling the best
+    at fixed caps of 4-32 resident workgroups per CU, its ceiling the best
     of them.  "adamw_in_place" is the headline update's own pattern -- four
     streams in the bucket placement, three of them written back in place --
     and is the ceiling the roofline is compared with; "amsgrad_in_place"

@@ -439,8 +439,11 @@ int radamw_fused_step_multi(const radamw_segment *segs, int32_t nseg,
                             radamw_stream_t stream, radamw_fused_result *result);
 
 /*
- * The fused step for callers that cannot allocate device memory: code under
- * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The fused step for callers that cannot allocate device memory: tight
+ * serving loops, harnesses that forbid hipMalloc, and programs that replay
+ * captured HIP graphs around it and may not allocate between replays.  The
+ * call itself waits for its stream (it reads the report back), so it cannot
+ * be recorded into a graph.
  * radamw_fused_step_multi over ONE flattened bucket (nseg <= 1; more is
  * RADAMW_ERR_RANGE) with no workspace argument: the statistics rows, merge
  * scratch, decision slot and report live in a static device array of the

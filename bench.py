@@ -17,10 +17,11 @@ give the kernel duration the roofline object uses.
 Prints ONE JSON line (rank 0).  Extra keys beside the contract's:
 "roofline" (with the update's fraction of the measured streaming ceiling),
 "cpu_baseline", "cpu_baseline_threads", "kernels" (update kernel timing, rest
-of the step), "stream_ceiling" (radamw_stream_probe: the update's access
-pattern with trivial arithmetic), "device" (GPU, versions, clocks from
-sysfs), "provenance" (command line, commit, source and library hashes),
-"variants" (update-only timings of the bucket's other configurations),
+of the step, the step timed as 7 samples of 20 steps), "stream_ceiling"
+(radamw_stream_probe: the update's access pattern with trivial arithmetic),
+"device" (GPU, versions, clocks from sysfs), "provenance" (command line,
+commit, source and library hashes), "variants" (update-only timings of the
+bucket's other configurations),
 "staged_vs_fused" (the pages' staged baseline A/B), "decoder_1b_list"
 (per-tensor launches, the multi-tensor call over the list, and one
 flattened bucket), "decoder_7b_fused_step" (the whole step over a
@@ -228,6 +229,21 @@ def main(argv=None):
                          f"{ex} merge level(s) + final merge, decision taken on the device by the final merge (the host reads the 12-byte report while the update runs), launch latencies",
                          "rows": rows_n, "extra_merge_kernels": ex},
     }
+    # after the timed region, the pages' timing shape: 7 samples of 20
+    # back-to-back steps, each sample between synchronisations
+    per_step = []
+    for _ in range(7):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(20):
+            one_step()
+        torch.cuda.synchronize()
+        per_step.append((time.perf_counter() - t1) * 1e3 / 20)
+    per_step.sort()
+    kernels["step_seven_samples_of_20"] = {"median_ms": per_step[3], "min_ms": per_step[0], "max_ms": per_step[-1],
+                                           "what": "wall clock per step, 7 samples of 20 steps, outside the "
+                                                   "timed region"}
+    log(f"step, 7 samples of 20: median {per_step[3]:.4f} ms [{per_step[0]:.4f}, {per_step[-1]:.4f}]")
     del p, g, m, v, ws, seglist
     torch.cuda.empty_cache()
 

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -59,14 +60,17 @@ struct DeviceCache {
     // pinned 12-byte staging for report read-back
     radamw_stats *pinned_report = nullptr;
     // host memory mapped for the device: the fused step's final merge writes
-    // its report (offset 0) and its decision (offset 16) here directly, so
-    // the read-back is only a wait for the merge (merge_done)
+    // its report (offset 0), its decision (offset 16) and then the call's
+    // sequence number (offset 32) here directly, so the read-back is the host
+    // watching that word (report_mu)
     std::mutex report_mu;
     radamw_stats *mapped_report_host = nullptr;
     radamw_stats *mapped_report_dev = nullptr;
     Decision *mapped_decision_host = nullptr;
     Decision *mapped_decision_dev = nullptr;
-    hipEvent_t merge_done = nullptr;
+    volatile uint32_t *mapped_done_host = nullptr;
+    uint32_t *mapped_done_dev = nullptr;
+    uint32_t done_seq = 0;
     // one merged record per list of a multi-list fused step (report_mu)
     StatsRec *group_rec = nullptr;
     int64_t group_cap = 0;
@@ -816,8 +820,7 @@ std::vector<char> build_stats_table(const std::vector<StatsSeg> &st, int64_t nro
 }
 
 // The per-device page of host memory mapped for the device, which receives
-// the final merge's report and decision, and the event that marks the
-// merge's completion (report_mu held).
+// the final merge's report, decision and completion word (report_mu held).
 int ensure_mapped(DeviceCache &dc, int dev) {
     if (dc.mapped_report_host) return RADAMW_OK;
     DeviceScope scope(dev);
@@ -825,16 +828,42 @@ int ensure_mapped(DeviceCache &dc, int dev) {
     hipError_t e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) return hip_status(e);
     e = hipHostGetDevicePointer(&dp, hp, 0);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&dc.merge_done, hipEventDisableTiming);
     if (e != hipSuccess) {
-        dc.merge_done = nullptr;
         (void)hipHostFree(hp);
         return hip_status(e);
     }
+    std::memset(hp, 0, 64);
     dc.mapped_report_host = static_cast<radamw_stats *>(hp);
     dc.mapped_report_dev = static_cast<radamw_stats *>(dp);
     dc.mapped_decision_host = reinterpret_cast<Decision *>(static_cast<char *>(hp) + 16);
     dc.mapped_decision_dev = reinterpret_cast<Decision *>(static_cast<char *>(dp) + 16);
+    dc.mapped_done_host = reinterpret_cast<volatile uint32_t *>(static_cast<char *>(hp) + 32);
+    dc.mapped_done_dev = reinterpret_cast<uint32_t *>(static_cast<char *>(dp) + 32);
+    return RADAMW_OK;
+}
+
+// Wait until the final merge of this call has written `seq` to the mapped
+// completion word.  A wait longer than WAIT_CHECK_PERIOD also asks the
+// stream, once per period, whether it can still get there: an error on the
+// stream, or a stream that has drained without the word, ends the wait with
+// an error.  (Asking on every wait would cost the GPU time: the runtime
+// answers a query on a busy stream by queueing a completion marker behind
+// its last kernel.)
+constexpr auto WAIT_CHECK_PERIOD = std::chrono::milliseconds(10);
+
+int wait_done(const DeviceCache &dc, uint32_t seq, hipStream_t stream) {
+    auto next_check = std::chrono::steady_clock::now() + WAIT_CHECK_PERIOD;
+    for (uint32_t i = 1;; ++i) {
+        if (*dc.mapped_done_host == seq) break;
+        __builtin_ia32_pause();
+        if ((i & 1023) == 0 && std::chrono::steady_clock::now() >= next_check) {
+            const hipError_t e = hipStreamQuery(stream);
+            if (e != hipSuccess && e != hipErrorNotReady) return hip_status(e);
+            if (e == hipSuccess && *dc.mapped_done_host != seq) return hip_status(hipErrorUnknown);
+            next_check = std::chrono::steady_clock::now() + WAIT_CHECK_PERIOD;
+        }
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
     return RADAMW_OK;
 }
 
@@ -843,10 +872,12 @@ int ensure_mapped(DeviceCache &dc, int dev) {
 //                          `cur` for the final merge;
 //   the final merge reduces them, takes the skip / clip decision on the
 //   device and writes report and decision into the mapped page, and the
-//   decision also to dec_dev, where the update kernels read it;
+//   decision also to dec_dev, where the update kernels read it; then it
+//   writes this call's sequence number to the page's completion word;
 //   submit()               queues the update launches right behind it;
-// only then does the host wait, for the merge alone, and read the page.  The
-// GPU goes from the merge to the updates without waiting for the host.
+// only then does the host wait, for the merge alone, by watching that word,
+// and read the page.  Nothing is queued between the merge and the updates,
+// so the GPU goes from one to the other without a gap.
 template <typename Prepare, typename Submit>
 int fused_tail(int dev, hipStream_t stream, Decision *dec_dev, const DecideArgs &args, radamw_stats *host,
                Decision *host_dec, Prepare prepare, Submit submit) {
@@ -857,15 +888,16 @@ int fused_tail(int dev, hipStream_t stream, Decision *dec_dev, const DecideArgs 
     const StatsRec *cur = nullptr;
     int64_t count = 0;
     if ((rc = prepare(&cur, &count))) return rc;
+    if (++dc.done_seq == 0) dc.done_seq = 1;  // the page starts at 0
+    DecideArgs a = args;
+    a.done = dc.mapped_done_dev;
+    a.seq = dc.done_seq;
     rc = hip_status(launch_merge_decide(cur, count, reinterpret_cast<StatsRec *>(dc.mapped_report_dev), dec_dev,
-                                        dc.mapped_decision_dev, args, stream));
+                                        dc.mapped_decision_dev, a, stream));
     if (rc) return rc;
     g_launches.fetch_add(1, std::memory_order_relaxed);
-    hipError_t e = hipEventRecord(dc.merge_done, stream);
-    if (e != hipSuccess) return hip_status(e);
     const int submitted = submit();
-    e = hipEventSynchronize(dc.merge_done);
-    if (e != hipSuccess) return hip_status(e);
+    if ((rc = wait_done(dc, a.seq, stream))) return rc;
     std::memcpy(host, dc.mapped_report_host, sizeof *host);
     std::memcpy(host_dec, dc.mapped_decision_host, sizeof *host_dec);
     return submitted;

@@ -187,10 +187,14 @@ static_assert(sizeof(Decision) == 8 && offsetof(Decision, inv_scale) == 4,
               "the update kernels load a decision as two 32-bit words");
 
 // What the final merge needs to decide: the caller's scale and the clip
-// bound (<= 0: no clipping).
+// bound (<= 0: no clipping); and, when `done` is set, the word of host
+// memory mapped for the device to which it writes `seq` once the report
+// and the decision are visible to the host.
 struct DecideArgs {
     double gradient_scale;
     double max_grad_norm;
+    uint32_t *done = nullptr;
+    uint32_t seq = 0;
 };
 
 // Global-address-space views of generic pointers.  Tensor pointers that

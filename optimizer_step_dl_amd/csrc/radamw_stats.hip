@@ -297,6 +297,12 @@ __global__ __launch_bounds__(MERGE_BLOCK) void stats_merge_decide(const StatsRec
             __builtin_bit_cast(double, uint64_t(rec.w[0]) | (uint64_t(rec.w[1]) << 32)), rec.w[2], a);
         *dec_dev = d;
         *dec_host = d;
+        if (a.done) {
+            // the host waits on this word: the report and the decision
+            // reach host memory first
+            __threadfence_system();
+            *reinterpret_cast<volatile uint32_t *>(a.done) = a.seq;
+        }
     }
 }
 

@@ -18,6 +18,7 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 using namespace radamw;
@@ -843,24 +844,37 @@ int ensure_mapped(DeviceCache &dc, int dev) {
 }
 
 // Wait until the final merge of this call has written `seq` to the mapped
-// completion word.  A wait longer than WAIT_CHECK_PERIOD also asks the
-// stream, once per period, whether it can still get there: an error on the
-// stream, or a stream that has drained without the word, ends the wait with
-// an error.  (Asking on every wait would cost the GPU time: the runtime
-// answers a query on a busy stream by queueing a completion marker behind
-// its last kernel.)
+// completion word.  The host spins for WAIT_SPIN, then yields its thread
+// between reads (a step called with a long backward pass still queued
+// would otherwise keep a core busy all along; the GPU has the update
+// kernels queued meanwhile, so a late return costs it nothing).  A wait
+// longer than WAIT_CHECK_PERIOD also asks the stream, once per period,
+// whether it can still get there: an error on the stream, or a stream that
+// has drained without the word, ends the wait with an error.  (Asking on
+// every wait would cost the GPU time: the runtime answers a query on a busy
+// stream by queueing a completion marker behind its last kernel.)
+constexpr auto WAIT_SPIN = std::chrono::milliseconds(1);
 constexpr auto WAIT_CHECK_PERIOD = std::chrono::milliseconds(10);
 
 int wait_done(const DeviceCache &dc, uint32_t seq, hipStream_t stream) {
-    auto next_check = std::chrono::steady_clock::now() + WAIT_CHECK_PERIOD;
+    const auto start = std::chrono::steady_clock::now();
+    auto next_check = start + WAIT_CHECK_PERIOD;
+    bool yield = false;
     for (uint32_t i = 1;; ++i) {
         if (*dc.mapped_done_host == seq) break;
-        __builtin_ia32_pause();
-        if ((i & 1023) == 0 && std::chrono::steady_clock::now() >= next_check) {
-            const hipError_t e = hipStreamQuery(stream);
-            if (e != hipSuccess && e != hipErrorNotReady) return hip_status(e);
-            if (e == hipSuccess && *dc.mapped_done_host != seq) return hip_status(hipErrorUnknown);
-            next_check = std::chrono::steady_clock::now() + WAIT_CHECK_PERIOD;
+        if (yield)
+            std::this_thread::yield();
+        else
+            __builtin_ia32_pause();
+        if ((i & 255) == 0) {
+            const auto now = std::chrono::steady_clock::now();
+            yield = yield || now - start >= WAIT_SPIN;
+            if (now >= next_check) {
+                const hipError_t e = hipStreamQuery(stream);
+                if (e != hipSuccess && e != hipErrorNotReady) return hip_status(e);
+                if (e == hipSuccess && *dc.mapped_done_host != seq) return hip_status(hipErrorUnknown);
+                next_check = std::chrono::steady_clock::now() + WAIT_CHECK_PERIOD;
+            }
         }
     }
     std::atomic_thread_fence(std::memory_order_acquire);

@@ -207,6 +207,19 @@ def test_fused_step_decision_slot_with_odd_rows_and_workspace_alignment():
     assert e.value.status == -4 and ra.radamw_launch_count() == before
 
 
+def test_fused_step_behind_queued_work():
+    """A fused step queued behind tens of milliseconds of other work on its
+    stream (torch's bounded busy kernel): the host spins, then yields, then
+    checks the stream now and then until the final merge writes this call's
+    completion word, and the step still returns the oracle's result.  Two
+    such steps in a row each wait for their own word."""
+    announce("fused step behind queued work")
+    for k in range(2):
+        torch.cuda._sleep(50_000_000)
+        res = _fused_case([4096, 300_000], "f32", 0, 0.05, (0, "fq", k))
+        assert res.updated and res.clip_coef < 1.0
+
+
 def test_fused_step_found_inf_skips_everything():
     announce("fused found_inf")
     res = _fused_case([4096, 1_000_000, 2049], "bf16", 3, 1.0, (0, "fi"), step0=4)

@@ -1,4 +1,6 @@
-"""Full-size GPU parity: the 2^28 bucket, the 1.1B-parameter 201-tensor list
+"""Full-size GPU parity: the 2^28 bucket (every update variant bench.py
+times, the first step, the write-back of a BF16 model copy and the fused
+step), the 1.1B-parameter 201-tensor list
 (as separate tensors and as one flattened bucket), the 6.7B-parameter
 291-tensor list with statistics, clipping and an injected non-finite step,
 and one tensor beyond 32-bit indexing.
@@ -11,7 +13,7 @@ the 1e-6 (1 + |ref|) contract on p, m, v, v_max and ulp bars on the
 moments).  Statistics are checked over every gradient element.
 
 Page abbreviations: FA-ja = "実験的なデバイス上の融合 AdamW / AMSGrad",
-TR-zh = "训练与状态保存"."""
+FA-zh = "实验性融合 AdamW / AMSGrad", TR-zh = "训练与状态保存"."""
 import numpy as np
 import pytest
 import torch
@@ -37,7 +39,7 @@ def _clone(ts):
 
 @pytest.mark.parametrize("variant,gdt,mode", [
     ("adamw", "f32", "inplace"), ("adamw", "f32", "outofplace"), ("amsgrad", "f32", "inplace"),
-    ("amsgrad", "f32", "outofplace"), ("adamw", "bf16", "inplace")])
+    ("amsgrad", "f32", "outofplace"), ("adamw", "bf16", "inplace"), ("amsgrad", "f16", "inplace")])
 def test_bucket_2pow28_steady_state(variant, gdt, mode):
     """The 268,435,456-element bucket at t = 1000 as bench.py builds it,
     updated the way bench.py's update-only variants launch it (one-segment
@@ -75,6 +77,69 @@ def test_bucket_2pow28_steady_state(variant, gdt, mode):
     announce(f"largest moment errors in units of their ulp bars: {stats}")
     if amsgrad:
         assert bool(torch.all(outs[3] >= outs[2]))
+
+
+def test_bucket_2pow28_first_step():
+    """The bucket's first step (no state: FA-zh "增加的实际能力"), as bench.py's
+    first-step variant launches it: m and v start as NaN-filled buffers, so
+    any read of them would poison the result; every element of p, m and v
+    against the oracle's first step."""
+    n = 1 << 28
+    announce("bucket 2^28 first step")
+    key = (0, "bucket", n)
+    p = synth.normal(n, 0.02, key + ("p",), DEV)
+    g = synth.stored_grad(n, 1e-3, 1.0, "f32", key + ("g",), DEV)
+    m = torch.full((n,), float("nan"), device=DEV)
+    v = torch.full((n,), float("nan"), device=DEV)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    pre = (p.clone(), m.clone(), v.clone(), None)
+    st = ra.AdamWState(0, m, v, None)
+    assert ra.radamw_step_inplace(p, g, st, opts, ra.control(1.0)) and st.step == 1
+    torch.cuda.synchronize()
+    stage = PinnedStage()
+    ref = oracle_one_step_pinned(stage, pre, g, "f32", oracle_opts(opts), 1.0, 0, False)
+    stats = {}
+    compare_one_step_full("bucket first step", (p, m, v, None), ref, pre, g, 1.0, 0.9, 0.999,
+                          first=True, power_of_two=True, stats=stats)
+    announce(f"largest moment errors in units of their ulp bars: {stats}")
+
+
+def test_bucket_2pow28_bf16_model_copy():
+    """The bucket's update with the BF16 model copy written in the same pass
+    (bench.py's write-back variant): p, m, v against the oracle element by
+    element; the copy equals torch's round-to-nearest-even conversion of the
+    updated p bit for bit, and the oracle's rounding of its own p within the
+    contract on p plus one BF16 unit."""
+    n = 1 << 28
+    announce("bucket 2^28 with BF16 model copy")
+    key = (0, "bucket", n)
+    p = synth.normal(n, 0.02, key + ("p",), DEV)
+    g = synth.stored_grad(n, 1e-3, 1.0, "f32", key + ("g",), DEV)
+    m, v, _ = synth.steady_state(n, key, False, DEV, m_std=1e-4, v_root_std=1e-3)
+    opts = ra.options(lr=1e-3, weight_decay=1e-4)
+    pre = _clone((p, m, v, None))
+    model = torch.full((n,), 7.0, dtype=torch.bfloat16, device=DEV)
+    updated, step = ra.radamw_step_multi_writeback([ra.Segment(p, g, m, v, None)], [model], 999, opts,
+                                                   ra.control(1.0))
+    assert updated and step == 1000
+    torch.cuda.synchronize()
+    assert torch.equal(model.view(torch.int16), p.to(torch.bfloat16).view(torch.int16))
+    stage = PinnedStage()
+    ref = oracle_one_step_pinned(stage, pre, g, "f32", oracle_opts(opts), 1.0, 999, False)
+    compare_one_step_full("bucket with model copy", (p, m, v, None), ref, pre, g, 1.0, 0.9, 0.999,
+                          first=False, power_of_two=True)
+    ref_bits = torch.from_numpy(oracle.round_copy(ref[0].numpy(), "bf16").view(np.int16))
+    chunk = 1 << 25
+    same = 0
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        ours = model[lo:hi].double()
+        want = ref_bits[lo:hi].to(DEV).view(torch.bfloat16).double()
+        p_ref = ref[0][lo:hi].to(DEV).double()
+        bound = 1e-6 * (1 + p_ref.abs()) + 2.0**-7 * p_ref.abs() + 2.0**-24
+        assert bool(torch.all((ours - want).abs() <= bound)), f"model copy, elements {lo}..{hi}"
+        same += int(torch.count_nonzero(ours == want))
+    assert same > 0.99 * n
 
 
 def test_bucket_2pow28_fused_step_as_benched():

@@ -33,7 +33,9 @@
  *     in host memory owned by the caller, and the bias-correction
  *     coefficients are computed on the host for every call, so a captured
  *     graph replay would repeat one step's coefficients (FA-zh
- *     "增加的实际能力"); graph capture is not supported.
+ *     "增加的实际能力"); graph capture is not supported: a stream being
+ *     captured is refused with RADAMW_ERR_INVALID before anything is
+ *     launched or recorded.
  *   - Thread safety: calls may come from several host threads; each call is
  *     independent apart from the launch counter and the per-device caches
  *     (segment-table staging, the mapped report page, the second update
@@ -60,7 +62,8 @@ enum {
                                 pointer of another device, an array running
                                 past the end of its allocation, hyper-
                                 parameter out of range, non-finite or
-                                non-positive gradient_scale, flag not 0/1     */
+                                non-positive gradient_scale, flag not 0/1,
+                                a stream being captured into a graph          */
     RADAMW_ERR_STATE = -2,   /* AMSGrad flag and v_max presence disagree, or
                                 the step count would overflow                 */
     RADAMW_ERR_ALIAS = -3,   /* a written range overlaps another range         */

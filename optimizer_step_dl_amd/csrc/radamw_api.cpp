@@ -126,14 +126,20 @@ struct DeviceScope {
     }
 };
 
+// The device of `stream`; a stream being captured into a graph is refused
+// (a replay would repeat one step's host-formed coefficients, and a fused
+// step waits for its own kernels, which a capture never runs).
 int stream_device(hipStream_t stream, int *dev) {
     hipDevice_t d = 0;
     hipError_t e = stream ? hipStreamGetDevice(stream, &d) : hipGetDevice(&d);
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (e == hipSuccess) e = hipStreamIsCapturing(stream, &capture);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         g_last_hip = static_cast<int>(e);
         return RADAMW_ERR_INVALID;
     }
+    if (capture != hipStreamCaptureStatusNone) return RADAMW_ERR_INVALID;
     if (d < 0 || d >= MAX_DEVICES) return RADAMW_ERR_INVALID;
     *dev = static_cast<int>(d);
     return RADAMW_OK;

@@ -638,6 +638,49 @@ def test_rejections_leave_everything_untouched():
     assert unchanged(before, [buf])
 
 
+def test_stream_under_graph_capture_is_refused():
+    """A stream being captured into a HIP graph is refused with
+    RADAMW_ERR_INVALID before anything is launched or recorded (a replay
+    would repeat one step's host-formed coefficients, and a fused step waits
+    for kernels a capture never runs): the in-place update, the fused step
+    and the statistics call each return the error inside a capture, and
+    nothing of theirs runs."""
+    announce("graph capture refused")
+    n = 4096
+    p, g = torch.zeros(n, device=DEV), torch.ones(n, device=DEV)
+    st = ra.AdamWState(1, torch.zeros(n, device=DEV), torch.zeros(n, device=DEV))
+    seg = [ra.Segment(p, g, st.exp_avg, st.exp_avg_sq)]
+    ws = torch.zeros(ra.radamw_fused_workspace_bytes(seg), dtype=torch.uint8, device=DEV)
+    rows = torch.empty(3 * 8, dtype=torch.int32, device=DEV)
+    marker = torch.zeros(16, device=DEV)
+    launches = ra.radamw_launch_count()
+    before = snapshot(p, st.exp_avg, st.exp_avg_sq)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    calls = (lambda: ra.radamw_step_inplace(p, g, st, ra.options(), ra.control()),
+             lambda: ra.radamw_fused_step_multi(seg, 1, ra.options(), 1.0, 1.0, True, ws),
+             lambda: ra.radamw_grad_stats(g, rows))
+    statuses = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        graph.capture_begin(capture_error_mode="relaxed")
+        try:
+            marker.add_(1.0)  # one node of torch's own, so the graph is not empty
+            for call in calls:
+                try:
+                    call()
+                    statuses.append(0)
+                except ra.RadamwError as e:
+                    statuses.append(e.status)
+        finally:
+            graph.capture_end()
+    torch.cuda.synchronize()
+    assert statuses == [-1, -1, -1]
+    assert ra.radamw_launch_count() == launches and st.step == 1
+    assert unchanged(before, [p, st.exp_avg, st.exp_avg_sq])
+    assert int(torch.count_nonzero(marker)) == 0  # captured, never replayed
+
+
 # ------------------------------------------------------- staged baseline --
 
 @pytest.mark.parametrize("gdt,amsgrad", [("f32", False), ("f32", True), ("bf16", True), ("f16", False)])
